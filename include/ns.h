@@ -1,0 +1,189 @@
+/*
+ * ns.h -- C ABI of the MI355X (gfx950) Newton-Schulz orthogonalisation library.
+ *
+ * The operation is the one defined on the DMuon documentation page
+ * "Newton-Schulz 变体" (Newton-Schulz variants):
+ *
+ *   - section "精度流水线" (precision pipeline): X = G / (||G||_F + eps) in
+ *     fp32, then X is cast to fp16 and iterated in fp16;
+ *   - section "直接空间 NS（经典）" (direct space): per step
+ *     X <- a_k X + b_k (X X^T) X + c_k (X X^T)^2 X on the full matrix;
+ *   - section "Gram 空间 NS（Dao-AILab）" (Gram space), equations Z_k and
+ *     Q_{k+1}: R = X X^T, Z_k = b_k R_k + c_k R_k^2,
+ *     Q_{k+1} = Z_k Q_k + a_k Q_k, R evolved by recurrence, output Q X;
+ *   - section "重启机制" (restart mechanism): before each listed step index
+ *     Q is applied to X and R is rebuilt from X;
+ *   - section "系数集" (coefficient sets): tables of (a_k, b_k, c_k) rows.
+ *
+ * The library computes on the short side: a matrix with more rows than
+ * columns is transposed on the way in and back on the way out, so every
+ * Gram matrix is min(m, n) square.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   Layout      Matrices are row-major: element (i, j) of an (m, n) matrix
+ *               with leading dimension ld sits at base[i * ld + j]
+ *               (ld counted in elements, ld >= n).
+ *   Ownership   Every device pointer (inputs, outputs, workspace) belongs to
+ *               the caller; the library never allocates or frees device
+ *               memory. Host arrays (coeffs, restarts, the ns_matrix array)
+ *               are read during the call only.
+ *   Streams     `stream` is a hipStream_t passed as void* (NULL = the null
+ *               stream). Calls enqueue work and return; results are valid
+ *               once the stream reaches them. Outputs must not overlap
+ *               inputs or the workspace. Concurrent calls on different
+ *               streams need different workspaces.
+ *   Errors      Return codes only: nothing is printed and nothing is thrown.
+ *               Argument checks run on the host before any device work; on
+ *               any error other than NS_ERR_HIP nothing has been enqueued.
+ *               NaN or Inf in the input propagate to the output.
+ *   Device      The current HIP device must be a gfx950 GPU, otherwise
+ *               NS_ERR_UNSUPPORTED.
+ *   Determinism The same inputs on the same device give bitwise identical
+ *               outputs: fixed tile and reduction order, no float atomics.
+ *   Precision   Every stored intermediate is fp16; products accumulate in
+ *               fp32; scalar epilogues are evaluated in fp32 and rounded
+ *               once.
+ */
+#ifndef NSMI_NS_H
+#define NSMI_NS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NS_OK = 0,
+  NS_ERR_INVALID_ARG = 1,  /* a size, pointer, dtype or parameter is invalid */
+  NS_ERR_UNSUPPORTED = 2,  /* no HIP device, or the device is not gfx950    */
+  NS_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required   */
+  NS_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed    */
+} ns_status;
+
+typedef enum { NS_DT_F32 = 0, NS_DT_BF16 = 1, NS_DT_F16 = 2 } ns_dtype;
+
+/* Axis 1 of the page's section "后端分发" (backend dispatch): the algorithm.
+ * Axis 2 (which SYRK kernel) has a single value here: this library's gfx950
+ * MFMA kernels. */
+typedef enum { NS_GRAM = 0, NS_DIRECT = 1 } ns_backend;
+
+#define NS_MAX_STEPS 16
+
+/* Iteration parameters (the page's NewtonSchulz(coefficients=...,
+ * restart_iterations=...) arguments plus the normalisation eps).
+ *   num_steps     K, 1 <= K <= NS_MAX_STEPS.
+ *   coeffs        host array of 3*K floats a_0, b_0, c_0, a_1, ...; row k is
+ *                 used at step k. Must be finite.
+ *   restarts      host array of num_restarts step indices in [0, K-1]
+ *                 (gram only, ignored by direct). Index 0 is a no-op,
+ *                 duplicates are ignored. May be NULL if num_restarts == 0.
+ *   eps           added to the Frobenius norm; finite and >= 0.            */
+typedef struct {
+  int num_steps;
+  const float* coeffs;
+  const int* restarts;
+  int num_restarts;
+  float eps;
+} ns_params;
+
+/* One matrix of a call.
+ *   g, g_dtype, m, n, ldg   input G (device), fp32 / bf16 / fp16, (m, n)
+ *                           row-major, m >= 1, n >= 1, ldg >= n.
+ *   out, out_dtype, ldo     output (device), same (m, n) orientation as G,
+ *                           fp16 (the iteration dtype) / bf16 / fp32 (both
+ *                           taken from the fp32 accumulator of the last
+ *                           product), ldo >= n.                              */
+typedef struct {
+  const void* g;
+  ns_dtype g_dtype;
+  int64_t m, n, ldg;
+  void* out;
+  ns_dtype out_dtype;
+  int64_t ldo;
+} ns_matrix;
+
+/* Largest side accepted for m or n. */
+#define NS_MAX_DIM 65536
+
+/* Bytes of device workspace that ns_gram / ns_direct / ns_batched need for
+ * these matrices (count >= 1; `mats[i].g/out` are not read). Pure host
+ * computation. Writes *bytes. */
+ns_status ns_workspace_size(const ns_matrix* mats, int count, ns_backend backend,
+                            const ns_params* params, size_t* bytes);
+
+/* Precision pipeline step 1 and 2 on one matrix: x = fp16(g / (||g||_F + eps))
+ * with the norm accumulated in fp32 and the quotient rounded to nearest even.
+ *   x, ldx           device output. If transpose_tall != 0 and m > n, x is
+ *                    the (n, m) transpose of the result (the short-side
+ *                    orientation the iteration uses); otherwise (m, n).
+ *                    ldx >= number of columns of x.
+ *   norm_out         device float receiving ||g||_F, or NULL.
+ *   ws, ws_bytes     device workspace of ns_normalize_workspace_size bytes.
+ */
+ns_status ns_normalize_workspace_size(int64_t m, int64_t n, size_t* bytes);
+ns_status ns_normalize(const void* g, ns_dtype g_dtype, int64_t m, int64_t n,
+                       int64_t ldg, void* x, int64_t ldx, int transpose_tall,
+                       float eps, float* norm_out, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* Direct-space NS on one matrix (the page's direct_newton_schulz /
+ * NewtonSchulz("direct")). Restarts in params are ignored. */
+ns_status ns_direct(const ns_matrix* mat, const ns_params* params, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* Gram-space NS on one matrix (the page's newton_schulz /
+ * NewtonSchulz("gram")), with restarts. */
+ns_status ns_gram(const ns_matrix* mat, const ns_params* params, void* ws,
+                  size_t ws_bytes, void* stream);
+
+/* NS on `count` independent matrices of mixed shapes, one kernel launch per
+ * stage over all of them (tiles of larger matrices scheduled first). Each
+ * output is bitwise equal to what ns_gram / ns_direct gives for that matrix
+ * alone. count == 0 is a no-op. `mats` is a host array. */
+ns_status ns_batched(const ns_matrix* mats, int count, ns_backend backend,
+                     const ns_params* params, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Building blocks of the iteration, exposed for kernel-level testing.
+ * All operands are fp16 row-major device matrices; products accumulate in
+ * fp32 and the scaled sum is rounded once to fp16.
+ *
+ * ns_syrk: r = x x^T for x (s, l); r is (s, s) with leading dimension s and
+ * is exactly symmetric (lower-triangle tiles computed, then mirrored). This
+ * is the Gram product R = X X^T of the page's Gram-space section.
+ * Requires s % 256 == 0 and l % 64 == 0 (dense: leading dims l and s).
+ *
+ * ns_gemm_nt: d = alpha * (a b^T) + beta * c + gamma * I for a (M, K) and
+ * b (N, K) (so b^T is K x N), c and d (M, N); c may be NULL when beta == 0.
+ * symmetric != 0 computes only the lower-triangle tiles (requires M == N)
+ * and mirrors them, so d is exactly symmetric; use it only when the result
+ * is symmetric in exact arithmetic. Requires M % 256 == 0, N % 256 == 0,
+ * K % 64 == 0, dense leading dimensions (K for a and b, N for c and d).
+ *
+ * Both take a device workspace of at least NS_UNIT_WORKSPACE_BYTES bytes
+ * (it holds the launch descriptor). */
+#define NS_UNIT_WORKSPACE_BYTES 4096
+ns_status ns_syrk(const void* x, int64_t s, int64_t l, void* r, void* ws,
+                  size_t ws_bytes, void* stream);
+ns_status ns_gemm_nt(const void* a, const void* b, const void* c, void* d,
+                     int64_t M, int64_t N, int64_t K, float alpha, float beta,
+                     float gamma, int symmetric, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Human-readable status name; never NULL. */
+const char* ns_status_string(ns_status s);
+
+/* One-line summary of the algorithm axis and kernel set for the current
+ * device (the counterpart of the page's get_ns_backend(), section
+ * "查询当前后端"), e.g. "Gram NS / direct NS · kernel=hip-mfma-f16
+ * (gfx950, 256 CUs)". Never NULL; valid until the next call. */
+const char* ns_backend_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSMI_NS_H */

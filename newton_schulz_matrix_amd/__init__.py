@@ -1,0 +1,331 @@
+"""Python binding of the gfx950 Newton-Schulz library (libnsmi.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/ns.h. PyTorch supplies device
+memory (outputs and workspaces) and the current stream. If the library is
+not built, importing works but every call raises.
+
+Names follow the C ABI: ``ns_normalize``, ``ns_gram``, ``ns_direct``,
+``ns_batched``, ``ns_workspace_size``, plus the building blocks ``ns_syrk``
+and ``ns_gemm_nt`` and the diagnostics ``ns_backend_info`` /
+``ns_status_string``.
+
+The coefficient tables are the two 5-step sets of the DMuon page
+"Newton-Schulz 变体", section "系数集" (coefficient sets), as printed there;
+the Polar Express set is the default and the default restart list is [2]
+(section "重启机制").
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Iterable, List, Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libnsmi.so")
+
+POLAR_EXPRESS_COEFFICIENTS = (
+    (7.893, -20.381, 14.939),
+    (3.912, -2.544, 0.470),
+    (3.761, -2.512, 0.476),
+    (3.160, -2.148, 0.440),
+    (2.191, -1.441, 0.361),
+)
+YOU_COEFFICIENTS = (
+    (4.0848, -6.8946, 2.9270),
+    (3.9505, -6.3029, 2.6377),
+    (3.7418, -5.5913, 2.3037),
+    (2.8769, -3.1427, 1.2046),
+    (2.8366, -3.0525, 1.2012),
+)
+COEFFICIENT_SETS = {"polar_express": POLAR_EXPRESS_COEFFICIENTS,
+                    "you": YOU_COEFFICIENTS}
+DEFAULT_RESTARTS = (2,)
+DEFAULT_EPS = 1e-7
+
+NS_OK, NS_ERR_INVALID_ARG, NS_ERR_UNSUPPORTED, NS_ERR_WORKSPACE, NS_ERR_HIP = range(5)
+NS_DT_F32, NS_DT_BF16, NS_DT_F16 = 0, 1, 2
+NS_GRAM, NS_DIRECT = 0, 1
+NS_UNIT_WORKSPACE_BYTES = 4096
+BACKENDS = {"gram": NS_GRAM, "direct": NS_DIRECT}
+
+
+class NsError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("num_steps", ctypes.c_int),
+                ("coeffs", ctypes.POINTER(ctypes.c_float)),
+                ("restarts", ctypes.POINTER(ctypes.c_int)),
+                ("num_restarts", ctypes.c_int),
+                ("eps", ctypes.c_float)]
+
+
+class _Matrix(ctypes.Structure):
+    _fields_ = [("g", ctypes.c_void_p),
+                ("g_dtype", ctypes.c_int),
+                ("m", ctypes.c_int64), ("n", ctypes.c_int64), ("ldg", ctypes.c_int64),
+                ("out", ctypes.c_void_p),
+                ("out_dtype", ctypes.c_int),
+                ("ldo", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libnsmi.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m newton_schulz_matrix_amd.build` (no CPU fallback exists)")
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+        P, M = ctypes.POINTER(_Params), ctypes.POINTER(_Matrix)
+        sigs = {
+            "ns_workspace_size": [M, ctypes.c_int, ctypes.c_int, P, ctypes.POINTER(sz)],
+            "ns_normalize_workspace_size": [i64, i64, ctypes.POINTER(sz)],
+            "ns_normalize": [vp, ctypes.c_int, i64, i64, i64, vp, i64, ctypes.c_int,
+                             ctypes.c_float, vp, vp, sz, vp],
+            "ns_direct": [M, P, vp, sz, vp],
+            "ns_gram": [M, P, vp, sz, vp],
+            "ns_batched": [M, ctypes.c_int, ctypes.c_int, P, vp, sz, vp],
+            "ns_syrk": [vp, i64, i64, vp, vp, sz, vp],
+            "ns_gemm_nt": [vp, vp, vp, vp, i64, i64, i64, ctypes.c_float, ctypes.c_float,
+                           ctypes.c_float, ctypes.c_int, vp, sz, vp],
+        }
+        for name, args in sigs.items():
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        lib.ns_status_string.argtypes = [ctypes.c_int]
+        lib.ns_status_string.restype = ctypes.c_char_p
+        lib.ns_backend_info.argtypes = []
+        lib.ns_backend_info.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return library().ns_status_string(status).decode()
+
+
+def ns_backend_info() -> str:
+    return library().ns_backend_info().decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != NS_OK:
+        raise NsError(status, where)
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dtype) -> int:
+    torch = _torch()
+    codes = {torch.float32: NS_DT_F32, torch.bfloat16: NS_DT_BF16,
+             torch.float16: NS_DT_F16}
+    if dtype not in codes:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return codes[dtype]
+
+
+def _rowmajor_ld(t) -> int:
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    if t.stride(1) != 1 and t.shape[1] > 1:
+        raise ValueError("rows must be contiguous (stride(1) == 1)")
+    return max(t.stride(0), t.shape[1]) if t.shape[0] > 1 else t.shape[1]
+
+
+def _device_tensor(t, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t
+
+
+def _stream_ptr(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _params(coefficients, restart_iterations, eps):
+    coeffs = [float(x) for row in coefficients for x in row]
+    if len(coeffs) % 3:
+        raise ValueError("coefficients must be rows of (a, b, c)")
+    rs = [int(i) for i in restart_iterations]
+    carr = (ctypes.c_float * max(1, len(coeffs)))(*coeffs)
+    rarr = (ctypes.c_int * max(1, len(rs)))(*rs)
+    p = _Params(len(coeffs) // 3, carr, rarr, len(rs), float(eps))
+    return p, (carr, rarr)  # keep the arrays alive
+
+
+def _matrix(G, out) -> _Matrix:
+    return _Matrix(G.data_ptr(), _dtype_code(G.dtype), G.shape[0], G.shape[1],
+                   _rowmajor_ld(G), out.data_ptr(), _dtype_code(out.dtype),
+                   _rowmajor_ld(out))
+
+
+def _workspace(nbytes: int, device):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def ns_workspace_size(shapes: Sequence[Sequence[int]], backend: str = "gram",
+                      coefficients=POLAR_EXPRESS_COEFFICIENTS,
+                      restart_iterations: Iterable[int] = DEFAULT_RESTARTS,
+                      eps: float = DEFAULT_EPS) -> int:
+    """Workspace bytes for matrices of the given (m, n) shapes."""
+    mats = (_Matrix * len(shapes))()
+    for i, (m, n) in enumerate(shapes):
+        mats[i] = _Matrix(None, NS_DT_F32, m, n, n, None, NS_DT_F16, n)
+    p, keep = _params(coefficients, restart_iterations, eps)
+    nbytes = ctypes.c_size_t(0)
+    _check(library().ns_workspace_size(mats, len(shapes), BACKENDS[backend],
+                                       ctypes.byref(p), ctypes.byref(nbytes)),
+           "ns_workspace_size")
+    return nbytes.value
+
+
+def ns_batched(Gs: List, backend: str = "gram",
+               coefficients=POLAR_EXPRESS_COEFFICIENTS,
+               restart_iterations: Iterable[int] = DEFAULT_RESTARTS,
+               eps: float = DEFAULT_EPS, out_dtype=None, outs: Optional[List] = None,
+               workspace=None) -> List:
+    """NS on a list of GPU matrices in one grouped call; returns the outputs."""
+    torch = _torch()
+    if len(Gs) == 0:
+        return []
+    dev = Gs[0].device
+    out_dtype = out_dtype or torch.float16
+    for G in Gs:
+        _device_tensor(G, "G")
+    if outs is None:
+        outs = [torch.empty(G.shape, dtype=out_dtype, device=dev) for G in Gs]
+    mats = (_Matrix * len(Gs))()
+    for i, (G, O) in enumerate(zip(Gs, outs)):
+        mats[i] = _matrix(G, _device_tensor(O, "out"))
+    p, keep = _params(coefficients, restart_iterations, eps)
+    lib = library()
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.ns_workspace_size(mats, len(Gs), BACKENDS[backend], ctypes.byref(p),
+                                 ctypes.byref(nbytes)), "ns_workspace_size")
+    if workspace is None or workspace.numel() < nbytes.value:
+        workspace = _workspace(nbytes.value, dev)
+    _check(lib.ns_batched(mats, len(Gs), BACKENDS[backend], ctypes.byref(p),
+                          workspace.data_ptr(), workspace.numel(), _stream_ptr(Gs[0])),
+           "ns_batched")
+    return outs
+
+
+def ns_gram(G, coefficients=POLAR_EXPRESS_COEFFICIENTS,
+            restart_iterations: Iterable[int] = DEFAULT_RESTARTS,
+            eps: float = DEFAULT_EPS, out_dtype=None, out=None, workspace=None):
+    """Gram-space NS of one GPU matrix (the page's newton_schulz)."""
+    torch = _torch()
+    _device_tensor(G, "G")
+    out = out if out is not None else torch.empty(
+        G.shape, dtype=out_dtype or torch.float16, device=G.device)
+    mat = _matrix(G, _device_tensor(out, "out"))
+    p, keep = _params(coefficients, restart_iterations, eps)
+    lib = library()
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.ns_workspace_size(ctypes.byref(mat), 1, NS_GRAM, ctypes.byref(p),
+                                 ctypes.byref(nbytes)), "ns_workspace_size")
+    if workspace is None or workspace.numel() < nbytes.value:
+        workspace = _workspace(nbytes.value, G.device)
+    _check(lib.ns_gram(ctypes.byref(mat), ctypes.byref(p), workspace.data_ptr(),
+                       workspace.numel(), _stream_ptr(G)), "ns_gram")
+    return out
+
+
+def ns_direct(G, coefficients=POLAR_EXPRESS_COEFFICIENTS, eps: float = DEFAULT_EPS,
+              out_dtype=None, out=None, workspace=None):
+    """Direct-space NS of one GPU matrix (the page's direct_newton_schulz)."""
+    torch = _torch()
+    _device_tensor(G, "G")
+    out = out if out is not None else torch.empty(
+        G.shape, dtype=out_dtype or torch.float16, device=G.device)
+    mat = _matrix(G, _device_tensor(out, "out"))
+    p, keep = _params(coefficients, (), eps)
+    lib = library()
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.ns_workspace_size(ctypes.byref(mat), 1, NS_DIRECT, ctypes.byref(p),
+                                 ctypes.byref(nbytes)), "ns_workspace_size")
+    if workspace is None or workspace.numel() < nbytes.value:
+        workspace = _workspace(nbytes.value, G.device)
+    _check(lib.ns_direct(ctypes.byref(mat), ctypes.byref(p), workspace.data_ptr(),
+                         workspace.numel(), _stream_ptr(G)), "ns_direct")
+    return out
+
+
+def ns_normalize(G, eps: float = DEFAULT_EPS, transpose_tall: bool = True,
+                 return_norm: bool = False):
+    """fp16(G / (||G||_F + eps)); tall inputs come back transposed."""
+    torch = _torch()
+    _device_tensor(G, "G")
+    m, n = G.shape
+    tr = transpose_tall and m > n
+    x = torch.empty((n, m) if tr else (m, n), dtype=torch.float16, device=G.device)
+    norm = torch.empty(1, dtype=torch.float32, device=G.device)
+    lib = library()
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.ns_normalize_workspace_size(m, n, ctypes.byref(nbytes)),
+           "ns_normalize_workspace_size")
+    ws = _workspace(nbytes.value, G.device)
+    _check(lib.ns_normalize(G.data_ptr(), _dtype_code(G.dtype), m, n, _rowmajor_ld(G),
+                            x.data_ptr(), x.shape[1], 1 if transpose_tall else 0,
+                            float(eps), norm.data_ptr(), ws.data_ptr(), ws.numel(),
+                            _stream_ptr(G)), "ns_normalize")
+    return (x, norm) if return_norm else x
+
+
+def ns_syrk(X):
+    """R = X X^T for an fp16 (s, l) GPU matrix (s % 256 == 0, l % 64 == 0)."""
+    torch = _torch()
+    _device_tensor(X, "X")
+    X = X.contiguous()
+    s, l = X.shape
+    R = torch.empty((s, s), dtype=torch.float16, device=X.device)
+    ws = _workspace(NS_UNIT_WORKSPACE_BYTES, X.device)
+    _check(library().ns_syrk(X.data_ptr(), s, l, R.data_ptr(), ws.data_ptr(), ws.numel(),
+                             _stream_ptr(X)), "ns_syrk")
+    return R
+
+
+def ns_gemm_nt(A, B, C=None, alpha: float = 1.0, beta: float = 0.0,
+               gamma: float = 0.0, symmetric: bool = False):
+    """alpha A B^T + beta C + gamma I on fp16 GPU matrices."""
+    torch = _torch()
+    A, B = _device_tensor(A, "A").contiguous(), _device_tensor(B, "B").contiguous()
+    M, K = A.shape
+    N = B.shape[0]
+    D = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    cptr = C.contiguous().data_ptr() if C is not None else None
+    ws = _workspace(NS_UNIT_WORKSPACE_BYTES, A.device)
+    _check(library().ns_gemm_nt(A.data_ptr(), B.data_ptr(), cptr, D.data_ptr(), M, N, K,
+                                alpha, beta, gamma, 1 if symmetric else 0, ws.data_ptr(),
+                                ws.numel(), _stream_ptr(A)), "ns_gemm_nt")
+    return D
+
+
+def newton_schulz(G, backend: str = "gram", coefficients=POLAR_EXPRESS_COEFFICIENTS,
+                  restart_iterations: Iterable[int] = DEFAULT_RESTARTS,
+                  eps: float = DEFAULT_EPS, out_dtype=None):
+    """Dispatch on the page's algorithm axis ("gram" or "direct")."""
+    if backend == "gram":
+        return ns_gram(G, coefficients, restart_iterations, eps, out_dtype)
+    if backend == "direct":
+        return ns_direct(G, coefficients, eps, out_dtype)
+    raise ValueError(f"unknown backend {backend!r}")

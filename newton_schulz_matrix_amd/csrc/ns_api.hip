@@ -1,0 +1,709 @@
+// C ABI of the Newton-Schulz library: argument checks, workspace planning,
+// stage scheduling and launches. See include/ns.h for the contract.
+//
+// The stage sequence follows the "Newton-Schulz 变体" page:
+//   precision pipeline (section "精度流水线"): norm, scale, fp16 cast;
+//   Gram space (section "Gram 空间 NS", equations Z_k and Q_{k+1}) with the
+//   restart rule of section "重启机制"; or direct space (section
+//   "直接空间 NS"). Every stage is one grouped launch over all matrices of
+//   the call. Descriptor tables for all stages are built on the host and
+//   copied once per call into the tail of the caller's workspace.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/ns.h"
+#include "ns_internal.h"
+
+#define NS_API extern "C" __attribute__((visibility("default")))
+
+namespace nsmi {
+namespace {
+
+constexpr size_t ALIGN = 256;
+inline size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
+inline int64_t pad_dim(int64_t x) { return (x + PAD - 1) / PAD * PAD; }
+inline int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
+
+bool dtype_ok(ns_dtype t) { return t == NS_DT_F32 || t == NS_DT_BF16 || t == NS_DT_F16; }
+int out_code(ns_dtype t) { return t == NS_DT_F32 ? OUT_F32 : (t == NS_DT_BF16 ? OUT_BF16 : OUT_F16); }
+
+// ----------------------------------------------------------------- device
+
+enum DevState : int { DEV_UNKNOWN = 0, DEV_OK = 1, DEV_BAD = 2 };
+std::mutex g_dev_mu;
+std::map<int, int> g_dev_state;
+std::map<int, int> g_dev_cus;
+
+ns_status check_device() {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return NS_ERR_UNSUPPORTED;
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return NS_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  int& st = g_dev_state[dev];
+  if (st == DEV_UNKNOWN) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return NS_ERR_UNSUPPORTED;
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? DEV_OK : DEV_BAD;
+    g_dev_cus[dev] = prop.multiProcessorCount;
+  }
+  return st == DEV_OK ? NS_OK : NS_ERR_UNSUPPORTED;
+}
+
+// ---------------------------------------------------------------- upload
+// Descriptor tables are copied from a pinned host staging ring (so the copy
+// is truly asynchronous and the source stays valid until it runs). A slot
+// is reused only after the copy recorded on it has completed.
+
+struct Slot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+constexpr int RING = 8;
+struct Ring {
+  Slot slot[RING];
+  int next = 0;
+};
+std::mutex g_up_mu;
+std::map<int, Ring> g_rings;
+
+hipError_t upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_up_mu);
+  Ring& ring = g_rings[dev];
+  Slot& s = ring.slot[ring.next];
+  ring.next = (ring.next + 1) % RING;
+  if (s.pending) {
+    e = hipEventSynchronize(s.ev);
+    if (e != hipSuccess) return e;
+    s.pending = false;
+  }
+  if (!s.ev) {
+    e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+  }
+  if (s.cap < bytes) {
+    if (s.host) (void)hipHostFree(s.host);
+    s.host = nullptr;
+    s.cap = 0;
+    const size_t cap = std::max<size_t>(align_up(bytes, 65536), 65536);
+    e = hipHostMalloc(&s.host, cap, hipHostMallocPortable);
+    if (e != hipSuccess) return e;
+    s.cap = cap;
+  }
+  std::memcpy(s.host, src, bytes);
+  e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(s.ev, stream);
+  if (e != hipSuccess) return e;
+  s.pending = true;
+  return hipSuccess;
+}
+
+// ----------------------------------------------------------------- checks
+
+ns_status check_params(const ns_params* p, ns_backend be) {
+  if (!p) return NS_ERR_INVALID_ARG;
+  if (p->num_steps < 1 || p->num_steps > NS_MAX_STEPS) return NS_ERR_INVALID_ARG;
+  if (!p->coeffs) return NS_ERR_INVALID_ARG;
+  for (int i = 0; i < 3 * p->num_steps; ++i)
+    if (!std::isfinite(p->coeffs[i])) return NS_ERR_INVALID_ARG;
+  if (!std::isfinite(p->eps) || p->eps < 0.f) return NS_ERR_INVALID_ARG;
+  if (p->num_restarts < 0) return NS_ERR_INVALID_ARG;
+  if (p->num_restarts > 0 && !p->restarts) return NS_ERR_INVALID_ARG;
+  if (be == NS_GRAM) {
+    for (int i = 0; i < p->num_restarts; ++i)
+      if (p->restarts[i] < 0 || p->restarts[i] >= p->num_steps) return NS_ERR_INVALID_ARG;
+  }
+  return NS_OK;
+}
+
+ns_status check_matrix_shape(const ns_matrix& a) {
+  if (a.m < 1 || a.n < 1 || a.m > NS_MAX_DIM || a.n > NS_MAX_DIM) return NS_ERR_INVALID_ARG;
+  if (a.ldg < a.n || a.ldo < a.n) return NS_ERR_INVALID_ARG;
+  if (!dtype_ok(a.g_dtype) || !dtype_ok(a.out_dtype)) return NS_ERR_INVALID_ARG;
+  return NS_OK;
+}
+
+ns_status check_matrix(const ns_matrix& a) {
+  if (!a.g || !a.out) return NS_ERR_INVALID_ARG;
+  return check_matrix_shape(a);
+}
+
+// ----------------------------------------------------------------- planning
+
+struct Stage {
+  enum Kind { SUMSQ, FINALIZE, CAST, GEMM } kind;
+  size_t off;   // byte offset of its descriptors inside the table
+  int count;    // descriptors
+  int total;    // workgroups (chunks / tiles)
+};
+
+struct MatBuf {   // per-matrix workspace offsets (bytes from ws base)
+  int64_t m, n, s, l, Sp, Lp;
+  bool tall;
+  size_t X, XT[2], R, Z, T, Q[2], A, B;
+  int chunks, chunks_n, chunk_begin;
+};
+
+struct Plan {
+  std::vector<MatBuf> mats;
+  std::vector<int> order;          // matrices, largest first
+  size_t partials_off = 0, norms_off = 0, table_off = 0, total = 0;
+  int total_chunks = 0;
+  std::vector<Stage> stages;
+  std::vector<unsigned char> table;
+};
+
+size_t sq_bytes(int64_t r, int64_t c) { return static_cast<size_t>(r) * c * 2; }
+
+// Workspace layout: per-matrix fp16 buffers, chunk partials, norms, then
+// the descriptor table (its size depends only on count and params).
+void layout(Plan& pl, const ns_matrix* mats, int count, ns_backend be) {
+  size_t off = 0;
+  pl.mats.resize(count);
+  int chunk_begin = 0;
+  for (int i = 0; i < count; ++i) {
+    MatBuf& b = pl.mats[i];
+    b.m = mats[i].m;
+    b.n = mats[i].n;
+    b.tall = b.m > b.n;
+    b.s = std::min(b.m, b.n);
+    b.l = std::max(b.m, b.n);
+    b.Sp = pad_dim(b.s);
+    b.Lp = pad_dim(b.l);
+    const size_t xl = sq_bytes(b.Sp, b.Lp), ss = sq_bytes(b.Sp, b.Sp);
+    b.X = off; off += xl;
+    b.XT[0] = off; off += xl;
+    b.XT[1] = off; off += xl;
+    if (be == NS_GRAM) {
+      b.R = off; off += ss;
+      b.Z = off; off += ss;
+      b.T = off; off += ss;
+      b.Q[0] = off; off += ss;
+      b.Q[1] = off; off += ss;
+    } else {
+      b.A = off; off += ss;
+      b.B = off; off += ss;
+    }
+    b.chunks_n = ceil_div(b.n, SQ_COLS);
+    b.chunks = ceil_div(b.m, SQ_ROWS) * b.chunks_n;
+    b.chunk_begin = chunk_begin;
+    chunk_begin += b.chunks;
+  }
+  pl.total_chunks = chunk_begin;
+  pl.partials_off = align_up(off);
+  off = pl.partials_off + static_cast<size_t>(chunk_begin) * sizeof(float);
+  pl.norms_off = align_up(off);
+  off = pl.norms_off + static_cast<size_t>(count) * sizeof(float);
+  pl.table_off = align_up(off);
+  pl.order.resize(count);
+  for (int i = 0; i < count; ++i) pl.order[i] = i;
+  std::stable_sort(pl.order.begin(), pl.order.end(), [&](int a, int b) {
+    const MatBuf &x = pl.mats[a], &y = pl.mats[b];
+    if (x.Sp != y.Sp) return x.Sp > y.Sp;
+    return x.Lp > y.Lp;
+  });
+}
+
+struct Builder {
+  Plan& pl;
+  unsigned char* ws;   // device base (may be null while sizing)
+  explicit Builder(Plan& p, unsigned char* w) : pl(p), ws(w) {}
+
+  _Float16* h(size_t off) const { return reinterpret_cast<_Float16*>(ws + off); }
+
+  template <class D>
+  void push(Stage::Kind kind, std::vector<D>& v, int total) {
+    if (v.empty()) return;
+    Stage st;
+    st.kind = kind;
+    st.off = align_up(pl.table.size(), 64);
+    st.count = static_cast<int>(v.size());
+    st.total = total;
+    pl.table.resize(st.off + v.size() * sizeof(D));
+    std::memcpy(pl.table.data() + st.off, v.data(), v.size() * sizeof(D));
+    pl.stages.push_back(st);
+  }
+
+  // One grouped GEMM launch; problems ordered by tile cost (K), largest
+  // first, so long tiles start early and short ones fill the tail.
+  void gemm_stage(std::vector<GemmDesc> v) {
+    std::stable_sort(v.begin(), v.end(), [](const GemmDesc& a, const GemmDesc& b) {
+      if (a.K != b.K) return a.K > b.K;
+      return a.tiles > b.tiles;
+    });
+    int begin = 0;
+    for (auto& d : v) {
+      d.tile_begin = begin;
+      begin += d.tiles;
+    }
+    push(Stage::GEMM, v, begin);
+  }
+};
+
+GemmDesc gemm(const _Float16* A, const _Float16* B, const _Float16* C, void* D,
+              _Float16* D2, _Float16* DT, int64_t M, int64_t N, int64_t K, int64_t ldd,
+              int64_t valid_m, int64_t valid_n, int64_t diag_n, int out_type, bool sym,
+              float alpha, float beta, float gamma, float delta) {
+  GemmDesc d{};
+  const int T = gemm_tile();
+  d.A = A; d.B = B; d.C = C; d.D = D; d.D2 = D2; d.DT = DT;
+  d.M = static_cast<int>(M); d.N = static_cast<int>(N); d.K = static_cast<int>(K);
+  d.ldd = static_cast<int>(ldd);
+  d.valid_m = static_cast<int>(valid_m); d.valid_n = static_cast<int>(valid_n);
+  d.diag_n = static_cast<int>(diag_n);
+  d.out_type = out_type;
+  d.symmetric = sym ? 1 : 0;
+  if (sym) {
+    const int t = static_cast<int>(M / T);
+    d.tiles_n = t;
+    d.tiles = t * (t + 1) / 2;
+  } else {
+    d.tiles_n = static_cast<int>(N / T);
+    d.tiles = static_cast<int>((M / T) * (N / T));
+  }
+  d.alpha = alpha; d.beta = beta; d.gamma = gamma; d.delta = delta;
+  return d;
+}
+
+// Precision pipeline for every matrix: sum of squares, norm, scaled cast
+// into X (short side first) and X^T, zero-padded.
+void norm_stages(Builder& B, const ns_matrix* mats, float eps) {
+  Plan& pl = B.pl;
+  std::vector<NormDesc> v;
+  int tile_begin = 0;
+  for (int i : pl.order) {
+    const MatBuf& b = pl.mats[i];
+    NormDesc d{};
+    d.G = mats[i].g;
+    d.ldg = mats[i].ldg;
+    d.g_type = out_code(mats[i].g_dtype);
+    d.m = static_cast<int>(b.m);
+    d.n = static_cast<int>(b.n);
+    if (!b.tall) {   // G is already short side first: G -> X, G^T -> X^T
+      d.pm = static_cast<int>(b.Sp); d.pn = static_cast<int>(b.Lp);
+      d.P = B.h(b.X); d.ldp = b.Lp;
+      d.PT = B.h(b.XT[0]); d.ldpt = b.Sp;
+    } else {         // tall: G -> X^T, G^T -> X
+      d.pm = static_cast<int>(b.Lp); d.pn = static_cast<int>(b.Sp);
+      d.P = B.h(b.XT[0]); d.ldp = b.Sp;
+      d.PT = B.h(b.X); d.ldpt = b.Lp;
+    }
+    d.eps = eps;
+    d.norm_out = nullptr;
+    d.norm_slot = reinterpret_cast<float*>(B.ws + pl.norms_off) + i;
+    d.partials = reinterpret_cast<float*>(B.ws + pl.partials_off);
+    d.chunk_begin = b.chunk_begin;
+    d.chunks = b.chunks;
+    d.chunks_n = b.chunks_n;
+    d.tiles_n = ceil_div(d.pn, CAST_TILE);
+    d.tiles = ceil_div(d.pm, CAST_TILE) * d.tiles_n;
+    d.tile_begin = tile_begin;
+    tile_begin += d.tiles;
+    v.push_back(d);
+  }
+  // sumsq chunks are indexed by the chunk_begin of the matrix order in the
+  // layout; re-sort the descriptor copy for the chunk search.
+  std::vector<NormDesc> by_chunk = v;
+  std::sort(by_chunk.begin(), by_chunk.end(),
+            [](const NormDesc& a, const NormDesc& b) { return a.chunk_begin < b.chunk_begin; });
+  B.push(Stage::SUMSQ, by_chunk, pl.total_chunks);
+  B.push(Stage::FINALIZE, v, static_cast<int>(v.size()));
+  B.push(Stage::CAST, v, tile_begin);
+}
+
+void final_output(Builder& B, const ns_matrix& mt, const MatBuf& b, const _Float16* Qm,
+                  const _Float16* XT, const _Float16* Xc, const _Float16* XTc, float beta,
+                  std::vector<GemmDesc>& out) {
+  // wide: out = Q X = Q (X^T)^T                    (M = Sp, N = Lp)
+  // tall: out = (Q X)^T = X^T Q^T = X^T Q (Q sym.)  (M = Lp, N = Sp)
+  // (direct backend: Q is the step matrix b A + c A^2 and the epilogue adds
+  //  beta times X or X^T)
+  const int ot = out_code(mt.out_dtype);
+  if (!b.tall) {
+    out.push_back(gemm(Qm, XT, Xc, mt.out, nullptr, nullptr, b.Sp, b.Lp, b.Sp, mt.ldo, b.m,
+                       b.n, 0, ot, false, 1.f, beta, 0.f, 0.f));
+  } else {
+    out.push_back(gemm(XT, Qm, XTc, mt.out, nullptr, nullptr, b.Lp, b.Sp, b.Sp, mt.ldo, b.m,
+                       b.n, 0, ot, false, 1.f, beta, 0.f, 0.f));
+  }
+}
+
+void gram_stages(Builder& B, const ns_matrix* mats, const ns_params& p) {
+  Plan& pl = B.pl;
+  const int K = p.num_steps;
+  std::vector<bool> restart(K, false);
+  for (int i = 0; i < p.num_restarts; ++i) restart[p.restarts[i]] = true;
+
+  auto syrk_all = [&](int /*unused*/) {
+    std::vector<GemmDesc> v;
+    for (int i : pl.order) {
+      const MatBuf& b = pl.mats[i];
+      v.push_back(gemm(B.h(b.X), B.h(b.X), nullptr, B.h(b.R), nullptr, nullptr, b.Sp, b.Sp,
+                       b.Lp, b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, 0.f, 0.f, 0.f));
+    }
+    B.gemm_stage(v);
+  };
+
+  norm_stages(B, mats, p.eps);
+  syrk_all(0);
+  bool q_identity = true;
+  int qc = 0, xt = 0;
+  for (int k = 0; k < K; ++k) {
+    const float a = p.coeffs[3 * k], bk = p.coeffs[3 * k + 1], ck = p.coeffs[3 * k + 2];
+    if (restart[k] && !q_identity) {
+      // restart: X <- Q X (also written transposed), R <- X X^T, Q <- I
+      std::vector<GemmDesc> v;
+      for (int i : pl.order) {
+        const MatBuf& b = pl.mats[i];
+        v.push_back(gemm(B.h(b.Q[qc]), B.h(b.XT[xt]), nullptr, B.h(b.X), nullptr,
+                         B.h(b.XT[xt ^ 1]), b.Sp, b.Lp, b.Sp, b.Lp, b.Sp, b.Lp, 0, OUT_F16,
+                         false, 1.f, 0.f, 0.f, 0.f));
+      }
+      B.gemm_stage(v);
+      xt ^= 1;
+      syrk_all(0);
+      q_identity = true;
+    }
+    const bool need_r = (k + 1 < K) && !restart[k + 1];
+    // Z = b R + c R^2 (and, right after a start or restart, Q = Z + a I)
+    {
+      std::vector<GemmDesc> v;
+      for (int i : pl.order) {
+        const MatBuf& b = pl.mats[i];
+        _Float16* q2 = q_identity ? B.h(b.Q[qc ^ 1]) : nullptr;
+        v.push_back(gemm(B.h(b.R), B.h(b.R), B.h(b.R), B.h(b.Z), q2, nullptr, b.Sp, b.Sp, b.Sp,
+                         b.Sp, b.Sp, b.Sp, b.s, OUT_F16, true, ck, bk, 0.f, a));
+      }
+      B.gemm_stage(v);
+    }
+    // Q <- Z Q + a Q  and  T = Z R + a R  (both read Z; one launch)
+    {
+      std::vector<GemmDesc> v;
+      for (int i : pl.order) {
+        const MatBuf& b = pl.mats[i];
+        if (!q_identity)
+          v.push_back(gemm(B.h(b.Z), B.h(b.Q[qc]), B.h(b.Q[qc]), B.h(b.Q[qc ^ 1]), nullptr,
+                           nullptr, b.Sp, b.Sp, b.Sp, b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f,
+                           a, 0.f, 0.f));
+        if (need_r)
+          v.push_back(gemm(B.h(b.Z), B.h(b.R), B.h(b.R), B.h(b.T), nullptr, nullptr, b.Sp,
+                           b.Sp, b.Sp, b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, a, 0.f, 0.f));
+      }
+      B.gemm_stage(v);
+    }
+    qc ^= 1;
+    q_identity = false;
+    // R <- T Z + a T   (R_{k+1} = (a I + Z) R (a I + Z))
+    if (need_r) {
+      std::vector<GemmDesc> v;
+      for (int i : pl.order) {
+        const MatBuf& b = pl.mats[i];
+        v.push_back(gemm(B.h(b.T), B.h(b.Z), B.h(b.T), B.h(b.R), nullptr, nullptr, b.Sp, b.Sp,
+                         b.Sp, b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, a, 0.f, 0.f));
+      }
+      B.gemm_stage(v);
+    }
+  }
+  std::vector<GemmDesc> v;
+  for (int i : pl.order) {
+    const MatBuf& b = pl.mats[i];
+    final_output(B, mats[i], b, B.h(b.Q[qc]), B.h(b.XT[xt]), nullptr, nullptr, 0.f, v);
+  }
+  B.gemm_stage(v);
+}
+
+void direct_stages(Builder& B, const ns_matrix* mats, const ns_params& p) {
+  Plan& pl = B.pl;
+  const int K = p.num_steps;
+  norm_stages(B, mats, p.eps);
+  int xt = 0;
+  for (int k = 0; k < K; ++k) {
+    const float a = p.coeffs[3 * k], bk = p.coeffs[3 * k + 1], ck = p.coeffs[3 * k + 2];
+    std::vector<GemmDesc> v1, v2, v3;
+    for (int i : pl.order) {
+      const MatBuf& b = pl.mats[i];
+      // A = X X^T
+      v1.push_back(gemm(B.h(b.X), B.h(b.X), nullptr, B.h(b.A), nullptr, nullptr, b.Sp, b.Sp,
+                        b.Lp, b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, 0.f, 0.f, 0.f));
+      // B = b A + c A^2
+      v2.push_back(gemm(B.h(b.A), B.h(b.A), B.h(b.A), B.h(b.B), nullptr, nullptr, b.Sp, b.Sp,
+                        b.Sp, b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, ck, bk, 0.f, 0.f));
+      // X <- a X + B X  (in place; X^T written to the other buffer)
+      if (k + 1 < K) {
+        v3.push_back(gemm(B.h(b.B), B.h(b.XT[xt]), B.h(b.X), B.h(b.X), nullptr,
+                          B.h(b.XT[xt ^ 1]), b.Sp, b.Lp, b.Sp, b.Lp, b.Sp, b.Lp, 0, OUT_F16,
+                          false, 1.f, a, 0.f, 0.f));
+      } else {
+        final_output(B, mats[i], b, B.h(b.B), B.h(b.XT[xt]), B.h(b.X), B.h(b.XT[xt]), a, v3);
+      }
+    }
+    B.gemm_stage(v1);
+    B.gemm_stage(v2);
+    B.gemm_stage(v3);
+    xt ^= 1;
+  }
+}
+
+ns_status build_plan(Plan& pl, const ns_matrix* mats, int count, ns_backend be,
+                     const ns_params& p, unsigned char* ws) {
+  layout(pl, mats, count, be);
+  Builder B(pl, ws);
+  if (be == NS_GRAM) gram_stages(B, mats, p);
+  else direct_stages(B, mats, p);
+  pl.total = align_up(pl.table_off + pl.table.size());
+  return NS_OK;
+}
+
+ns_status run_plan(const Plan& pl, unsigned char* ws, hipStream_t stream) {
+  unsigned char* table = ws + pl.table_off;
+  if (upload(table, pl.table.data(), pl.table.size(), stream) != hipSuccess) return NS_ERR_HIP;
+  for (const Stage& st : pl.stages) {
+    hipError_t e = hipSuccess;
+    switch (st.kind) {
+      case Stage::SUMSQ:
+        e = launch_sumsq(reinterpret_cast<const NormDesc*>(table + st.off), st.count, st.total,
+                         stream);
+        break;
+      case Stage::FINALIZE:
+        e = launch_norm_finalize(reinterpret_cast<const NormDesc*>(table + st.off), st.count,
+                                 stream);
+        break;
+      case Stage::CAST:
+        e = launch_cast(reinterpret_cast<const NormDesc*>(table + st.off), st.count, st.total,
+                        stream);
+        break;
+      case Stage::GEMM:
+        e = launch_gemm(reinterpret_cast<const GemmDesc*>(table + st.off), st.count, st.total,
+                        stream);
+        break;
+    }
+    if (e != hipSuccess) return NS_ERR_HIP;
+  }
+  return NS_OK;
+}
+
+ns_status check_call(const ns_matrix* mats, int count, ns_backend be, const ns_params* p) {
+  if (count < 0) return NS_ERR_INVALID_ARG;
+  if (be != NS_GRAM && be != NS_DIRECT) return NS_ERR_INVALID_ARG;
+  ns_status s = check_params(p, be);
+  if (s != NS_OK) return s;
+  if (count > 0 && !mats) return NS_ERR_INVALID_ARG;
+  for (int i = 0; i < count; ++i) {
+    s = check_matrix(mats[i]);
+    if (s != NS_OK) return s;
+  }
+  return NS_OK;
+}
+
+ns_status run_batched(const ns_matrix* mats, int count, ns_backend be, const ns_params* p,
+                      void* ws, size_t ws_bytes, void* stream) {
+  ns_status s = check_call(mats, count, be, p);
+  if (s != NS_OK) return s;
+  if (count == 0) return NS_OK;
+  Plan sizing;
+  build_plan(sizing, mats, count, be, *p, nullptr);
+  if (!ws || ws_bytes < sizing.total) return NS_ERR_WORKSPACE;
+  s = check_device();
+  if (s != NS_OK) return s;
+  Plan pl;
+  build_plan(pl, mats, count, be, *p, static_cast<unsigned char*>(ws));
+  return run_plan(pl, static_cast<unsigned char*>(ws), static_cast<hipStream_t>(stream));
+}
+
+std::string g_info;
+
+}  // namespace
+}  // namespace nsmi
+
+using namespace nsmi;
+
+NS_API const char* ns_status_string(ns_status s) {
+  switch (s) {
+    case NS_OK: return "NS_OK";
+    case NS_ERR_INVALID_ARG: return "NS_ERR_INVALID_ARG";
+    case NS_ERR_UNSUPPORTED: return "NS_ERR_UNSUPPORTED";
+    case NS_ERR_WORKSPACE: return "NS_ERR_WORKSPACE";
+    case NS_ERR_HIP: return "NS_ERR_HIP";
+  }
+  return "NS_ERR_UNKNOWN";
+}
+
+NS_API const char* ns_backend_info(void) {
+  char buf[256];
+  if (check_device() == NS_OK) {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    int cus = 0;
+    {
+      std::lock_guard<std::mutex> lock(g_dev_mu);
+      cus = g_dev_cus[dev];
+    }
+    std::snprintf(buf, sizeof(buf),
+                  "Gram NS / direct NS · kernel=hip-mfma-f16 %dx%d tiles (gfx950, device %d, "
+                  "%d CUs)",
+                  gemm_tile(), gemm_tile(), dev, cus);
+  } else {
+    std::snprintf(buf, sizeof(buf),
+                  "Gram NS / direct NS · kernel=hip-mfma-f16 (no gfx950 device available)");
+  }
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  g_info = buf;
+  return g_info.c_str();
+}
+
+NS_API ns_status ns_workspace_size(const ns_matrix* mats, int count, ns_backend backend,
+                                   const ns_params* params, size_t* bytes) {
+  if (!bytes || count < 1 || !mats) return NS_ERR_INVALID_ARG;
+  if (backend != NS_GRAM && backend != NS_DIRECT) return NS_ERR_INVALID_ARG;
+  ns_status s = check_params(params, backend);
+  if (s != NS_OK) return s;
+  for (int i = 0; i < count; ++i) {
+    s = check_matrix_shape(mats[i]);
+    if (s != NS_OK) return s;
+  }
+  Plan pl;
+  build_plan(pl, mats, count, backend, *params, nullptr);
+  *bytes = pl.total;
+  return NS_OK;
+}
+
+NS_API ns_status ns_gram(const ns_matrix* mat, const ns_params* params, void* ws,
+                         size_t ws_bytes, void* stream) {
+  if (!mat) return NS_ERR_INVALID_ARG;
+  return run_batched(mat, 1, NS_GRAM, params, ws, ws_bytes, stream);
+}
+
+NS_API ns_status ns_direct(const ns_matrix* mat, const ns_params* params, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!mat) return NS_ERR_INVALID_ARG;
+  return run_batched(mat, 1, NS_DIRECT, params, ws, ws_bytes, stream);
+}
+
+NS_API ns_status ns_batched(const ns_matrix* mats, int count, ns_backend backend,
+                            const ns_params* params, void* ws, size_t ws_bytes, void* stream) {
+  return run_batched(mats, count, backend, params, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------- normalize
+
+namespace nsmi {
+namespace {
+struct NormPlan {
+  size_t partials_off, slot_off, desc_off, total;
+  int chunks, chunks_n;
+};
+NormPlan norm_plan(int64_t m, int64_t n) {
+  NormPlan p;
+  p.chunks_n = ceil_div(n, SQ_COLS);
+  p.chunks = ceil_div(m, SQ_ROWS) * p.chunks_n;
+  p.partials_off = 0;
+  p.slot_off = align_up(static_cast<size_t>(p.chunks) * sizeof(float));
+  p.desc_off = align_up(p.slot_off + sizeof(float));
+  p.total = align_up(p.desc_off + sizeof(NormDesc));
+  return p;
+}
+}  // namespace
+}  // namespace nsmi
+
+NS_API ns_status ns_normalize_workspace_size(int64_t m, int64_t n, size_t* bytes) {
+  if (!bytes || m < 1 || n < 1 || m > NS_MAX_DIM || n > NS_MAX_DIM) return NS_ERR_INVALID_ARG;
+  *bytes = norm_plan(m, n).total;
+  return NS_OK;
+}
+
+NS_API ns_status ns_normalize(const void* g, ns_dtype g_dtype, int64_t m, int64_t n, int64_t ldg,
+                              void* x, int64_t ldx, int transpose_tall, float eps,
+                              float* norm_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!g || !x) return NS_ERR_INVALID_ARG;
+  if (m < 1 || n < 1 || m > NS_MAX_DIM || n > NS_MAX_DIM || ldg < n) return NS_ERR_INVALID_ARG;
+  if (!dtype_ok(g_dtype)) return NS_ERR_INVALID_ARG;
+  if (!std::isfinite(eps) || eps < 0.f) return NS_ERR_INVALID_ARG;
+  const bool tr = transpose_tall && m > n;
+  if (ldx < (tr ? m : n)) return NS_ERR_INVALID_ARG;
+  const NormPlan np = norm_plan(m, n);
+  if (!ws || ws_bytes < np.total) return NS_ERR_WORKSPACE;
+  ns_status s = check_device();
+  if (s != NS_OK) return s;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  NormDesc d{};
+  d.G = g;
+  d.ldg = ldg;
+  d.g_type = out_code(g_dtype);
+  d.m = static_cast<int>(m);
+  d.n = static_cast<int>(n);
+  d.pm = static_cast<int>(m);
+  d.pn = static_cast<int>(n);
+  if (tr) {
+    d.PT = static_cast<_Float16*>(x);
+    d.ldpt = ldx;
+  } else {
+    d.P = static_cast<_Float16*>(x);
+    d.ldp = ldx;
+  }
+  d.eps = eps;
+  d.norm_out = norm_out;
+  d.norm_slot = reinterpret_cast<float*>(w + np.slot_off);
+  d.partials = reinterpret_cast<float*>(w + np.partials_off);
+  d.chunk_begin = 0;
+  d.chunks = np.chunks;
+  d.chunks_n = np.chunks_n;
+  d.tiles_n = ceil_div(n, CAST_TILE);
+  d.tiles = ceil_div(m, CAST_TILE) * d.tiles_n;
+  d.tile_begin = 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  NormDesc* dd = reinterpret_cast<NormDesc*>(w + np.desc_off);
+  if (upload(dd, &d, sizeof(d), st) != hipSuccess) return NS_ERR_HIP;
+  if (launch_sumsq(dd, 1, np.chunks, st) != hipSuccess) return NS_ERR_HIP;
+  if (launch_norm_finalize(dd, 1, st) != hipSuccess) return NS_ERR_HIP;
+  if (launch_cast(dd, 1, d.tiles, st) != hipSuccess) return NS_ERR_HIP;
+  return NS_OK;
+}
+
+// ---------------------------------------------------------- building blocks
+
+NS_API ns_status ns_gemm_nt(const void* a, const void* b, const void* c, void* d, int64_t M,
+                            int64_t N, int64_t K, float alpha, float beta, float gamma,
+                            int symmetric, void* ws, size_t ws_bytes, void* stream) {
+  if (!a || !b || !d) return NS_ERR_INVALID_ARG;
+  if (M < PAD || N < PAD || K < 64 || M % PAD || N % PAD || K % 64) return NS_ERR_INVALID_ARG;
+  if (M > NS_MAX_DIM || N > NS_MAX_DIM || K > NS_MAX_DIM) return NS_ERR_INVALID_ARG;
+  if (symmetric && M != N) return NS_ERR_INVALID_ARG;
+  if (!c && beta != 0.f) return NS_ERR_INVALID_ARG;
+  if (!std::isfinite(alpha) || !std::isfinite(beta) || !std::isfinite(gamma))
+    return NS_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < NS_UNIT_WORKSPACE_BYTES) return NS_ERR_WORKSPACE;
+  ns_status s = check_device();
+  if (s != NS_OK) return s;
+  GemmDesc g = gemm(static_cast<const _Float16*>(a), static_cast<const _Float16*>(b),
+                    static_cast<const _Float16*>(c), d, nullptr, nullptr, M, N, K, N, M, N,
+                    std::min(M, N), OUT_F16, symmetric != 0, alpha, c ? beta : 0.f, gamma, 0.f);
+  g.tile_begin = 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (upload(ws, &g, sizeof(g), st) != hipSuccess) return NS_ERR_HIP;
+  if (launch_gemm(static_cast<const GemmDesc*>(ws), 1, g.tiles, st) != hipSuccess)
+    return NS_ERR_HIP;
+  return NS_OK;
+}
+
+NS_API ns_status ns_syrk(const void* x, int64_t s, int64_t l, void* r, void* ws,
+                         size_t ws_bytes, void* stream) {
+  if (!x || !r) return NS_ERR_INVALID_ARG;
+  return ns_gemm_nt(x, x, nullptr, r, s, s, l, 1.f, 0.f, 0.f, 1, ws, ws_bytes, stream);
+}

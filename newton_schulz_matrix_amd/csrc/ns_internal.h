@@ -1,0 +1,93 @@
+// Internal descriptors shared by the host planner (ns_api.hip) and the
+// kernels (norm_kernels.hip, gemm_kernels.hip). Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nsmi {
+
+// Every internal matrix side is padded with zeros to a multiple of PAD so
+// that the GEMM kernels never need bounds checks in their main loops. Zero
+// padding is exact for this method: the padded rows/columns of X, R, Z, T
+// and Q stay zero (diagonal terms are applied only inside the real size).
+constexpr int PAD = 256;
+
+// Output element types (match ns_dtype values of the public header).
+enum OutType : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
+
+// GEMM problem "NT": acc = A * B^T with A (M x K) and B (N x K) row-major
+// fp16, leading dimension K for both. Epilogue, evaluated in fp32:
+//   v = alpha * acc + beta * C[i][j] + (i == j && i < diag_n ? gamma : 0)
+//   D[i][j]  = v                       (dtype out_type, leading dim ldd)
+//   D2[i][j] = v + (i == j && i < diag_n ? delta : 0)      (fp16, ld N)
+//   DT[j][i] = v                       (fp16, transposed, leading dim M)
+// Stores to D are clipped to i < valid_m, j < valid_n.
+// If symmetric: M == N, only tiles on or below the diagonal are computed
+// and every stored element (i, j), i >= j, is also stored at (j, i) in D
+// and D2, so both come out exactly symmetric.
+struct GemmDesc {
+  const _Float16* A;
+  const _Float16* B;
+  const _Float16* C;   // may alias D (same element read then written)
+  void* D;
+  _Float16* D2;        // optional
+  _Float16* DT;        // optional
+  int M, N, K;
+  int ldd;
+  int valid_m, valid_n;
+  int diag_n;
+  int out_type;
+  int symmetric;
+  int tile_begin;      // first logical tile of this problem in the launch
+  int tiles;           // number of tiles of this problem
+  int tiles_n;         // full: N / BN ; symmetric: M / BM
+  float alpha, beta, gamma, delta;
+};
+
+// Normalisation of one matrix G (m x n, leading dim ldg, dtype g_type):
+// x = fp16(g / (||G||_F + eps)). The padded region [0, pm) x [0, pn) in G's
+// orientation is written: P[i][j] (ld ldp) and/or PT[j][i] (ld ldpt), zero
+// outside the real m x n block.
+struct NormDesc {
+  const void* G;
+  int64_t ldg;
+  int g_type;          // OUT_F32 / OUT_BF16 / OUT_F16 encoding
+  int m, n;
+  int pm, pn;
+  _Float16* P;
+  int64_t ldp;
+  _Float16* PT;
+  int64_t ldpt;
+  float eps;
+  float* norm_out;     // optional copy of the norm (device)
+  float* norm_slot;    // where the finalize kernel stores the norm
+  float* partials;     // chunk partial sums of squares
+  int chunk_begin;     // first chunk of this matrix in the sumsq launch
+  int chunks;          // chunks of this matrix
+  int chunks_n;        // chunks along n
+  int tile_begin;      // first 64x64 tile of this matrix in the cast launch
+  int tiles;
+  int tiles_n;         // tiles along pn
+};
+
+// Sum-of-squares chunk: SQ_ROWS x SQ_COLS elements per workgroup.
+constexpr int SQ_ROWS = 32;
+constexpr int SQ_COLS = 256;
+// Cast tile.
+constexpr int CAST_TILE = 64;
+
+// Launchers (all enqueue on `stream`; return hipSuccess or the launch error).
+hipError_t launch_sumsq(const NormDesc* descs, int count, int total_chunks,
+                        hipStream_t stream);
+hipError_t launch_norm_finalize(const NormDesc* descs, int count,
+                                hipStream_t stream);
+hipError_t launch_cast(const NormDesc* descs, int count, int total_tiles,
+                       hipStream_t stream);
+hipError_t launch_gemm(const GemmDesc* descs, int count, int total_tiles,
+                       hipStream_t stream);
+
+// Tile edge of the GEMM kernel (BM == BN).
+int gemm_tile();
+
+}  // namespace nsmi

