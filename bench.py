@@ -1,0 +1,235 @@
+"""Throughput of owner-rank Newton-Schulz on one MI355X.
+
+Workload: one owner rank's share of a 32-layer Llama-3-8B over 8 owner slots,
+i.e. the seven projection shapes four times each (28 matrices, bf16 N(0, 1)
+synthetic gradients), run through one grouped ns_batched call per step:
+fp32 Frobenius normalisation, fp16 cast, five Gram-space NS steps with the
+Polar Express table and a restart before step 2. The direct backend is timed
+on the same batch as a second line of the report.
+
+One step = one full ns_batched call over all 28 matrices, inputs resident in
+HBM. Prints one JSON line.
+
+The roofline object describes the dominant kernel (the grouped MFMA GEMM):
+its algorithmic flops per launch (symmetric products counted at s (s + 1) k,
+general ones at 2 m n k; zero padding excluded) divided by its average launch
+duration, both measured inside the timed region with HIP events that the
+library records around each of its launches on the caller's stream.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2500.0     # MI355X dense fp16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+METRIC = "NS matrices/s + TFLOP/s (% fp16 MFMA peak), Llama-8B owner batch"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--backend", choices=["gram", "direct"], default="gram",
+                    help="headline backend")
+    ap.add_argument("--no-second-backend", action="store_true",
+                    help="time only the headline backend")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=25.0,
+                    help="seconds of oracle work for the CPU baseline sample")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def time_backend(nsmi, torch, Gs, outs, backend, table, restarts, steps, warmup):
+    """Warm up, then time exactly `steps` grouped calls; returns a dict."""
+    ws = torch.empty(nsmi.ns_workspace_size([tuple(G.shape) for G in Gs], backend, table,
+                                            restarts), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        nsmi.ns_batched(Gs, backend, table, restarts, outs=outs, workspace=ws)
+    torch.cuda.synchronize()
+    nsmi.ns_timing_enable(True)
+    nsmi.ns_timing_read()  # clear
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        nsmi.ns_batched(Gs, backend, table, restarts, outs=outs, workspace=ws)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nsmi.ns_timing_enable(False)
+    rep = nsmi.ns_timing_read()
+    ms = start.elapsed_time(end) / steps
+    del ws
+    return {"ms_per_step": ms, "wall_s": wall, "timing": rep}
+
+
+def cpu_baseline(workload, restarts, budget_s):
+    """The fp64 oracle on a bounded sample: one matrix per distinct Gram shape."""
+    import numpy as np
+
+    import workloads as W
+    from oracle import COEFFICIENT_SETS, gram_newton_schulz
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 0) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [os.cpu_count()])
+    except Exception:  # pragma: no cover - informational only
+        threads = os.cpu_count()
+
+    w = W.WORKLOADS[workload]
+    table = COEFFICIENT_SETS[w.coefficients]   # the oracle's own copy of the table
+    classes = {}
+    for j, (m, n) in enumerate(w.shapes):
+        key = (min(m, n), max(m, n))
+        classes.setdefault(key, []).append(j)
+    # cheapest class first; oracle flops of one gram call (full fp64 products)
+    def oracle_flops(s, l):
+        k = len(table)
+        r = len([i for i in set(restarts) if 0 < i < k])
+        return (1 + r) * 2.0 * s * s * l + (r + 1) * 2.0 * s * s * l + 4 * k * 2.0 * s ** 3
+
+    order = sorted(classes, key=lambda c: oracle_flops(*c))
+    measured, spent, rate = {}, 0.0, None
+    for key in order:
+        est = oracle_flops(*key) / rate if rate else 0.0
+        if measured and spent + est > budget_s:
+            break
+        j = classes[key][0]
+        G = W.matrix(workload, j).float().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        gram_newton_schulz(G, table, restarts)
+        dt = time.perf_counter() - t0
+        spent += dt
+        measured[key] = dt
+        rate = oracle_flops(*key) / dt
+        log(f"cpu oracle {key[0]}x{key[1]}: {dt:.2f} s ({rate / 1e9:.1f} GFLOP/s fp64)")
+    total = 0.0
+    for key, js in classes.items():
+        t = measured.get(key, oracle_flops(*key) / rate)
+        total += t * len(js)
+    sample = ("fp64 numpy oracle (gram backend, same table and restarts) timed on one matrix "
+              "of each Gram shape class " + ", ".join(f"{s}x{l}" for s, l in measured) +
+              "; whole-batch time = sum over the batch of the measured per-class time"
+              + ("" if len(measured) == len(classes) else
+                 "; unmeasured classes scaled by fp64 flop count"))
+    return {"value": len(w.shapes) / total, "unit": "matrices/s", "cores": int(threads),
+            "kind": "oracle", "sample": sample, "batch_seconds_est": total,
+            "sample_seconds": spent, "cpu_count": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); the owner-"
+              "rank Newton-Schulz path has no cross-GPU step to measure here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import newton_schulz_matrix_amd as nsmi
+    import workloads as W
+
+    nsmi.library()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    w = W.WORKLOADS[args.workload]
+    table = nsmi.COEFFICIENT_SETS[w.coefficients]
+    restarts = w.restarts
+    log(nsmi.ns_backend_info())
+    t0 = time.perf_counter()
+    Gs = []
+    for j in range(len(w.shapes)):
+        Gs.append(W.matrix(args.workload, j).cuda())
+    torch.cuda.synchronize()
+    log(f"inputs: {len(Gs)} matrices generated in {time.perf_counter() - t0:.1f} s")
+    outs = [torch.empty(G.shape, dtype=torch.float16, device="cuda") for G in Gs]
+
+    backends = [args.backend]
+    if not args.no_second_backend:
+        backends.append("direct" if args.backend == "gram" else "gram")
+    results = {}
+    for be in backends:
+        steps = args.steps if be == args.backend else max(1, min(args.steps, 3))
+        r = time_backend(nsmi, torch, Gs, outs, be, table, restarts, steps,
+                         args.warmup if be == args.backend else 1)
+        r["steps"] = steps
+        results[be] = r
+        t = r["timing"]
+        log(f"{be}: {r['ms_per_step']:.3f} ms/step, gemm {t['gemm_ms'] / steps:.3f} ms/step in "
+            f"{t['gemm_launches'] // steps} launches, norm {t['norm_ms'] / steps:.3f} ms/step")
+
+    head = results[args.backend]
+    K = head["steps"]
+    t = head["timing"]
+    ms = head["ms_per_step"]
+    n = len(Gs)
+    flops_step = (t["gemm_flops"]) / K
+    tflops = flops_step / (ms * 1e-3) / 1e12
+    avg_launch_ms = t["gemm_ms"] / t["gemm_launches"]
+    flops_per_launch = t["gemm_flops"] / t["gemm_launches"]
+    achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": n / (ms * 1e-3),
+        "unit": "matrices/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"Llama-3-8B owner share: 28 projections (4 x q/k/v/o/gate/up/"
+                               f"down), bf16 N(0,1) gradients, one ns_batched call",
+                   "matrices": n, "backend": args.backend, "coefficients": w.coefficients,
+                   "restarts": list(restarts), "eps": 1e-7, "input_dtype": w.dtype,
+                   "output_dtype": "f16"},
+        "tflops": tflops,
+        "pct_fp16_peak": 100.0 * tflops / PEAK_FP16_TFLOPS,
+        "flops_per_step": flops_step,
+        "roofline": {"bound": "mfma", "kernel": "gemm_nt_kernel (grouped fp16 MFMA)",
+                     "achieved": achieved, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP16_TFLOPS, "traffic": None,
+                     "launches_per_step": t["gemm_launches"] // K,
+                     "avg_launch_ms": avg_launch_ms,
+                     "flops_per_launch": flops_per_launch},
+        "norm_pass": {"ms_per_step": t["norm_ms"] / K,
+                      "bytes_per_step": t["norm_bytes"] / K,
+                      "gbs": (t["norm_bytes"] / K) / max(t["norm_ms"] / K * 1e-3, 1e-12) / 1e9,
+                      "peak_gbs": PEAK_HBM_GBS},
+    }
+    for be, r in results.items():
+        if be == args.backend:
+            continue
+        tt = r["timing"]
+        out[f"{be}_backend"] = {
+            "ms_per_step": r["ms_per_step"], "steps": r["steps"],
+            "matrices_per_s": n / (r["ms_per_step"] * 1e-3),
+            "tflops": tt["gemm_flops"] / r["steps"] / (r["ms_per_step"] * 1e-3) / 1e12}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.workload, restarts, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

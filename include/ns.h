@@ -154,14 +154,14 @@ ns_status ns_batched(const ns_matrix* mats, int count, ns_backend backend,
  * ns_syrk: r = x x^T for x (s, l); r is (s, s) with leading dimension s and
  * is exactly symmetric (lower-triangle tiles computed, then mirrored). This
  * is the Gram product R = X X^T of the page's Gram-space section.
- * Requires s % 256 == 0 and l % 64 == 0 (dense: leading dims l and s).
+ * Requires s % 256 == 0 and l % 128 == 0 (dense: leading dims l and s).
  *
  * ns_gemm_nt: d = alpha * (a b^T) + beta * c + gamma * I for a (M, K) and
  * b (N, K) (so b^T is K x N), c and d (M, N); c may be NULL when beta == 0.
  * symmetric != 0 computes only the lower-triangle tiles (requires M == N)
  * and mirrors them, so d is exactly symmetric; use it only when the result
  * is symmetric in exact arithmetic. Requires M % 256 == 0, N % 256 == 0,
- * K % 64 == 0, dense leading dimensions (K for a and b, N for c and d).
+ * K % 128 == 0, dense leading dimensions (K for a and b, N for c and d).
  *
  * Both take a device workspace of at least NS_UNIT_WORKSPACE_BYTES bytes
  * (it holds the launch descriptor). */
@@ -172,6 +172,27 @@ ns_status ns_gemm_nt(const void* a, const void* b, const void* c, void* d,
                      int64_t M, int64_t N, int64_t K, float alpha, float beta,
                      float gamma, int symmetric, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* Kernel timing (measurement aid). While enabled, every launch made by
+ * ns_normalize / ns_gram / ns_direct / ns_batched is bracketed by two HIP
+ * events on the caller's stream. ns_timing_read waits for the recorded
+ * events, reports the totals since the last read, and clears them. The
+ * algorithmic work counts exclude zero padding:
+ *   gemm_flops   2 m n k per general product; s (s + 1) k per symmetric
+ *                product (SYRK and the Gram-space products);
+ *   norm_bytes   HBM bytes the normalisation must move: the input read
+ *                twice (norm pass, scale pass) and two fp16 copies written.
+ * Enabling or disabling is global to the process; disabled by default. */
+typedef struct {
+  double gemm_ms;
+  int64_t gemm_launches;
+  double gemm_flops;
+  double norm_ms;
+  int64_t norm_launches;
+  double norm_bytes;
+} ns_timing_report;
+ns_status ns_timing_enable(int enable);
+ns_status ns_timing_read(ns_timing_report* report);
 
 /* Human-readable status name; never NULL. */
 const char* ns_status_string(ns_status s);

@@ -65,6 +65,15 @@ class _Params(ctypes.Structure):
                 ("eps", ctypes.c_float)]
 
 
+class TimingReport(ctypes.Structure):
+    _fields_ = [("gemm_ms", ctypes.c_double), ("gemm_launches", ctypes.c_int64),
+                ("gemm_flops", ctypes.c_double), ("norm_ms", ctypes.c_double),
+                ("norm_launches", ctypes.c_int64), ("norm_bytes", ctypes.c_double)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
 class _Matrix(ctypes.Structure):
     _fields_ = [("g", ctypes.c_void_p),
                 ("g_dtype", ctypes.c_int),
@@ -104,6 +113,10 @@ def library() -> ctypes.CDLL:
             f = getattr(lib, name)
             f.argtypes = args
             f.restype = ctypes.c_int
+        lib.ns_timing_enable.argtypes = [ctypes.c_int]
+        lib.ns_timing_enable.restype = ctypes.c_int
+        lib.ns_timing_read.argtypes = [ctypes.POINTER(TimingReport)]
+        lib.ns_timing_read.restype = ctypes.c_int
         lib.ns_status_string.argtypes = [ctypes.c_int]
         lib.ns_status_string.restype = ctypes.c_char_p
         lib.ns_backend_info.argtypes = []
@@ -118,6 +131,18 @@ def status_string(status: int) -> str:
 
 def ns_backend_info() -> str:
     return library().ns_backend_info().decode()
+
+
+def ns_timing_enable(enable: bool = True) -> None:
+    """Bracket every library launch with HIP events (see ns_timing_read)."""
+    _check(library().ns_timing_enable(1 if enable else 0), "ns_timing_enable")
+
+
+def ns_timing_read() -> dict:
+    """Kernel time and algorithmic work recorded since the last read."""
+    r = TimingReport()
+    _check(library().ns_timing_read(ctypes.byref(r)), "ns_timing_read")
+    return r.as_dict()
 
 
 def _check(status: int, where: str) -> None:

@@ -19,14 +19,22 @@
 // T = Z R + a R, R <- T Z + a T, the restart and output products Q X, and
 // the direct-space step X <- a X + (b A + c A^2) X (section "直接空间 NS").
 //
-// Kernel structure: BM x BN x BK workgroup tile, waves of 64 lanes each
-// owning a WM x WN sub-tile built from 32x32x16 fp16 MFMAs; A and B tiles
-// double-buffered in LDS with an XOR swizzle of the 16-byte chunks (so the
-// 128-bit fragment reads of 8 consecutive rows hit distinct banks); global
-// loads of tile k+1 issued before the MFMAs of tile k. Workgroup ids are
-// remapped so each XCD (8 per MI355X, one L2 each) works on runs of 32
-// neighbouring tiles, which share operand panels in its L2.
+// Kernel structure (gfx950):
+//   * 256 x 256 workgroup tile, 8 waves (two per SIMD), each owning a
+//     128 x 64 sub-tile of 32x32x16 fp16 MFMAs with fp32 accumulators;
+//   * operand tiles move global -> LDS by the buffer-load-to-LDS path (no
+//     register staging), through a four-stage ring of 256 x 32 slices so
+//     that the slice three steps ahead is in flight while one is consumed;
+//   * LDS rows are 64 bytes; the 16-byte chunks are XOR-swizzled by
+//     (row / 4) % 4 so the 16 lanes served per cycle by a 128-bit LDS read
+//     (16 consecutive rows) hit 16 distinct bank groups;
+//   * per slice, all MFMA fragments are read first, then the 16 MFMAs run
+//     while the later reads are still landing;
+//   * workgroup ids are remapped so each XCD (8 per MI355X, one L2 each)
+//     works on runs of 32 neighbouring tiles that share operand panels.
 #include "ns_internal.h"
+
+#include <type_traits>
 
 namespace nsmi {
 namespace {
@@ -47,12 +55,52 @@ struct Cfg {
   static constexpr int KSTEPS = BK / 16;
   static constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;
   static_assert(BM == BN, "square tiles (symmetric mode mirrors tiles)");
-  static_assert(KCH == 8, "swizzle assumes 8 chunks per row");
+  static_assert(KCH == 4, "swizzle assumes 64-byte LDS rows");
   static_assert(A_LOADS * THREADS == BM * KCH, "A tile / thread mismatch");
   static_assert(B_LOADS * THREADS == BN * KCH, "B tile / thread mismatch");
 };
 
-using MainCfg = Cfg<128, 128, 64, 64, 64>;
+// Workgroup tile 256 x 256, K slices of 32, eight waves of 128 x 64.
+using MainCfg = Cfg<256, 256, 32, 128, 64>;
+constexpr int STAGES = 4;      // LDS ring depth (K must be a multiple of 4 * 32)
+
+// Physical 16-byte chunk of logical chunk c in LDS row `row` (64-byte rows).
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor (gfx9 layout): 48-bit base, stride 0, size in bytes;
+// reads past `bytes` return zero.
+__device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  i32x4 r = {static_cast<int>(static_cast<uint32_t>(a)),
+             static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffff),
+             static_cast<int>(bytes), 0x00020000};
+  return r;
+}
+
+// One wave-wide global -> LDS copy of 16 bytes per lane: lane i's bytes land
+// at LDS byte address lds_addr + 16 i. Written as inline assembly so that
+// the only waits on it are the explicit vmcnt waits of the main loop (the
+// compiler would otherwise wait for every in-flight copy before any LDS
+// read). M0 is not used for anything else in this kernel.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff,
+                                           uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr_of(const _Float16* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const _Float16*)(p)));
+}
+
+// s_waitcnt immediate (gfx9): vmcnt in bits [3:0] and [15:14]; expcnt and
+// lgkmcnt left at their maxima, i.e. only vector-memory completions waited.
+constexpr int vmcnt_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 // Workgroup id -> logical tile. Hardware hands workgroups to the 8 XCDs
 // round-robin (id % 8). Logical tiles are cut into chunks of 32; chunk c
@@ -125,11 +173,174 @@ __device__ __forceinline__ void store_out(void* D, int out_type, int64_t idx, fl
   }
 }
 
+// Compile-time loop: f(integral_constant<int, I>) for I in [B, E). Keeps
+// accumulator indices constant so the accumulators stay in registers.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+struct Epi {
+  float alpha, beta, gamma, delta;
+  const _Float16* C;
+  void* D;
+  _Float16* D2;
+  _Float16* DT;
+  int M, N, ldd, diag_n, valid_m, valid_n, out_type;
+  int row0, col0;   // this lane's first row / column inside the tile
+};
+
+// MFMA 32x32 output layout: register r of lane l holds row
+// 8*(r/4) + 4*(l/32) + r%4 and column l%32 of each 32x32 block. For block
+// (I, J) and register group g this lane owns rows rb .. rb+3 of column col.
+template <class Cf, int I, int J, int G>
+__device__ __forceinline__ void block_coords(const Epi& e, int& rb, int& col) {
+  rb = e.row0 + I * 32 + G * 8;
+  col = e.col0 + J * 32;
+}
+
+// v = alpha * acc + beta * C (+ gamma on the real diagonal), 4 rows.
+template <int G>
+__device__ __forceinline__ void epi_values(const floatx16& a, const Epi& e, int rb, int col,
+                                           float (&v)[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float x = e.alpha * a[G * 4 + q];
+    if (e.C) x += e.beta * static_cast<float>(gmem(e.C)[static_cast<int64_t>(rb + q) * e.N + col]);
+    if (rb + q == col && col < e.diag_n) x += e.gamma;
+    v[q] = x;
+  }
+}
+
+// Symmetric product, tile strictly below the diagonal: store (i, j) and
+// the mirror (j, i) of every element; no diagonal terms occur.
+template <class Cf, class Acc>
+__device__ __forceinline__ void epilogue_sym_offdiag(const Acc& acc, const Epi& e) {
+  _Float16* D = static_cast<_Float16*>(e.D);
+  static_for<0, Cf::FM>([&](auto I) {
+    static_for<0, Cf::FN>([&](auto J) {
+      const floatx16& a = acc[I][J];
+      static_for<0, 4>([&](auto G) {
+        int rb, col;
+        block_coords<Cf, I, J, G>(e, rb, col);
+        float v[4];
+        epi_values<G>(a, e, rb, col, v);
+        half4 hv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          hv[q] = static_cast<_Float16>(v[q]);
+          gmem(D)[static_cast<int64_t>(rb + q) * e.ldd + col] = hv[q];
+        }
+        *gmem(reinterpret_cast<half4*>(D + static_cast<int64_t>(col) * e.ldd + rb)) = hv;
+        if (e.D2) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) gmem(e.D2)[static_cast<int64_t>(rb + q) * e.N + col] = hv[q];
+          *gmem(reinterpret_cast<half4*>(e.D2 + static_cast<int64_t>(col) * e.N + rb)) = hv;
+        }
+      });
+    });
+  });
+}
+
+// Symmetric product, diagonal tile: elements on or below the diagonal are
+// stored at (i, j) and mirrored; the upper half is never taken from acc.
+template <class Cf, class Acc>
+__device__ __forceinline__ void epilogue_sym_diag(const Acc& acc, const Epi& e) {
+  _Float16* D = static_cast<_Float16*>(e.D);
+  static_for<0, Cf::FM>([&](auto I) {
+    static_for<0, Cf::FN>([&](auto J) {
+      const floatx16& a = acc[I][J];
+      static_for<0, 4>([&](auto G) {
+        int rb, col;
+        block_coords<Cf, I, J, G>(e, rb, col);
+        float v[4];
+        epi_values<G>(a, e, rb, col, v);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = rb + q;
+          if (row < col) continue;
+          const _Float16 h = static_cast<_Float16>(v[q]);
+          gmem(D)[static_cast<int64_t>(row) * e.ldd + col] = h;
+          if (row != col) gmem(D)[static_cast<int64_t>(col) * e.ldd + row] = h;
+          if (e.D2) {
+            const float y = v[q] + ((row == col && row < e.diag_n) ? e.delta : 0.f);
+            const _Float16 h2 = static_cast<_Float16>(y);
+            gmem(e.D2)[static_cast<int64_t>(row) * e.N + col] = h2;
+            if (row != col) gmem(e.D2)[static_cast<int64_t>(col) * e.N + row] = h2;
+          }
+        }
+      });
+    });
+  });
+}
+
+// General product into an internal fp16 buffer, optionally also written
+// transposed (DT, leading dimension M).
+template <class Cf, class Acc>
+__device__ __forceinline__ void epilogue_full_f16(const Acc& acc, const Epi& e) {
+  _Float16* D = static_cast<_Float16*>(e.D);
+  static_for<0, Cf::FM>([&](auto I) {
+    static_for<0, Cf::FN>([&](auto J) {
+      const floatx16& a = acc[I][J];
+      static_for<0, 4>([&](auto G) {
+        int rb, col;
+        block_coords<Cf, I, J, G>(e, rb, col);
+        float v[4];
+        epi_values<G>(a, e, rb, col, v);
+        half4 hv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          hv[q] = static_cast<_Float16>(v[q]);
+          gmem(D)[static_cast<int64_t>(rb + q) * e.ldd + col] = hv[q];
+        }
+        if (e.D2) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row = rb + q;
+            const float y = v[q] + ((row == col && row < e.diag_n) ? e.delta : 0.f);
+            gmem(e.D2)[static_cast<int64_t>(row) * e.N + col] = static_cast<_Float16>(y);
+          }
+        }
+        if (e.DT)
+          *gmem(reinterpret_cast<half4*>(e.DT + static_cast<int64_t>(col) * e.M + rb)) = hv;
+      });
+    });
+  });
+}
+
+// Final output: user buffer, dtype fp16 / bf16 / fp32, clipped to the real
+// (valid_m, valid_n) block.
+template <class Cf, class Acc>
+__device__ __forceinline__ void epilogue_output(const Acc& acc, const Epi& e) {
+  static_for<0, Cf::FM>([&](auto I) {
+    static_for<0, Cf::FN>([&](auto J) {
+      const floatx16& a = acc[I][J];
+      static_for<0, 4>([&](auto G) {
+        int rb, col;
+        block_coords<Cf, I, J, G>(e, rb, col);
+        float v[4];
+        epi_values<G>(a, e, rb, col, v);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (rb + q < e.valid_m && col < e.valid_n)
+            store_out(e.D, e.out_type, static_cast<int64_t>(rb + q) * e.ldd + col, v[q]);
+      });
+    });
+  });
+}
+
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
     const GemmDesc* __restrict__ descs, int count, int total_tiles) {
-  __shared__ __attribute__((aligned(16))) _Float16 sA[2][C::A_ELEMS];
-  __shared__ __attribute__((aligned(16))) _Float16 sB[2][C::B_ELEMS];
+#if defined(__HIP_DEVICE_COMPILE__)
+  // Four stages as distinct LDS objects (the loop below is unrolled by four).
+  __shared__ __attribute__((aligned(1024))) _Float16 sA0[C::A_ELEMS], sB0[C::B_ELEMS];
+  __shared__ __attribute__((aligned(1024))) _Float16 sA1[C::A_ELEMS], sB1[C::B_ELEMS];
+  __shared__ __attribute__((aligned(1024))) _Float16 sA2[C::A_ELEMS], sB2[C::B_ELEMS];
+  __shared__ __attribute__((aligned(1024))) _Float16 sA3[C::A_ELEMS], sB3[C::B_ELEMS];
 
   const int t_logical = xcd_remap(blockIdx.x, total_tiles);
   const int p = find_problem(descs, count, t_logical);
@@ -146,185 +357,125 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
-  // Buffer resources over this tile's A and B row panels: loads use 32-bit
-  // offsets from a scalar base, and anything past the panel reads as zero.
-  const uint32_t panel_bytes = static_cast<uint32_t>(C::BM) * K * 2u;
-  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<_Float16*>(d.A + static_cast<int64_t>(m0) * K), (short)0, panel_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<_Float16*>(d.B + static_cast<int64_t>(n0) * K), (short)0, panel_bytes, 0x00020000);
-
   floatx16 acc[C::FM][C::FN];
+  static_for<0, C::FM>([&](auto I) {
+    static_for<0, C::FN>([&](auto J) {
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[I][J][r] = 0.f;
+    });
+  });
 
-  // Per-thread 16-byte chunks of the A and B tiles: byte offset inside the
-  // panel (at k0 = 0) and LDS element offset (XOR-swizzled chunk).
-  uint32_t a_goff[C::A_LOADS], b_goff[C::B_LOADS];
-  int a_soff[C::A_LOADS], b_soff[C::B_LOADS];
-#pragma unroll
-  for (int l = 0; l < C::A_LOADS; ++l) {
-    const int c = tid + l * C::THREADS;
-    const int row = c / C::KCH, kc = c % C::KCH;
-    a_goff[l] = (static_cast<uint32_t>(row) * K + kc * 8) * 2u;
-    a_soff[l] = row * C::BK + ((kc ^ (row & 7)) * 8);
-  }
-#pragma unroll
-  for (int l = 0; l < C::B_LOADS; ++l) {
-    const int c = tid + l * C::THREADS;
-    const int row = c / C::KCH, kc = c % C::KCH;
-    b_goff[l] = (static_cast<uint32_t>(row) * K + kc * 8) * 2u;
-    b_soff[l] = row * C::BK + ((kc ^ (row & 7)) * 8);
-  }
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 ra[C::A_LOADS], rb[C::B_LOADS];
-#define NSMI_GLOAD(k0)                                                               \
-  do {                                                                               \
-    const int kb_ = (k0) * 2;                                                        \
-    _Pragma("unroll") for (int l = 0; l < C::A_LOADS; ++l) ra[l] =                   \
-        __builtin_amdgcn_raw_buffer_load_b128(rA, a_goff[l], kb_, 0);                \
-    _Pragma("unroll") for (int l = 0; l < C::B_LOADS; ++l) rb[l] =                   \
-        __builtin_amdgcn_raw_buffer_load_b128(rB, b_goff[l], kb_, 0);                \
-  } while (0)
-#define NSMI_SSTORE(s)                                                               \
-  do {                                                                               \
-    _Pragma("unroll") for (int l = 0; l < C::A_LOADS; ++l)                           \
-        *reinterpret_cast<u32x4*>(&sA[s][a_soff[l]]) = ra[l];                        \
-    _Pragma("unroll") for (int l = 0; l < C::B_LOADS; ++l)                           \
-        *reinterpret_cast<u32x4*>(&sB[s][b_soff[l]]) = rb[l];                        \
-  } while (0)
+  // Copies: each wave instruction fills 1 KB of LDS = 16 tile rows of 64
+  // bytes; lane l lands on row l/4, physical chunk l%4, so it fetches
+  // logical chunk (l%4) ^ swz(row) of that row. Offsets are relative to the
+  // tile's row panel; the K position goes in the scalar offset.
+  constexpr int NW = C::THREADS / 64;
+  constexpr int RPB = 1024 / (C::BK * 2);
+  constexpr int BLK_A = C::BM / RPB / NW, BLK_B = C::BN / RPB / NW;
+  const uint32_t panel_bytes = static_cast<uint32_t>(C::BM) * K * 2u;
+  const i32x4 rA = make_rsrc(d.A + static_cast<int64_t>(m0) * K, panel_bytes);
+  const i32x4 rB = make_rsrc(d.B + static_cast<int64_t>(n0) * K, panel_bytes);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t a_off[BLK_A], b_off[BLK_B];
+  static_for<0, BLK_A>([&](auto i) {
+    const int row = (wv * BLK_A + i) * RPB + lane / C::KCH;
+    a_off[i] = (static_cast<uint32_t>(row) * K + (((lane % C::KCH) ^ swz(row)) * 8)) * 2u;
+  });
+  static_for<0, BLK_B>([&](auto i) {
+    const int row = (wv * BLK_B + i) * RPB + lane / C::KCH;
+    b_off[i] = (static_cast<uint32_t>(row) * K + (((lane % C::KCH) ^ swz(row)) * 8)) * 2u;
+  });
+  auto load_slice = [&](_Float16* SA, _Float16* SB, int k0) {
+    const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
+    static_for<0, BLK_A>([&](auto i) {
+      lds_copy16(rA, lds_addr_of(SA + (wv * BLK_A + i) * 512), a_off[i], kb);
+    });
+    static_for<0, BLK_B>([&](auto i) {
+      lds_copy16(rB, lds_addr_of(SB + (wv * BLK_B + i) * 512), b_off[i], kb);
+    });
+    __builtin_amdgcn_sched_barrier(0);   // keep the copies at the top
+  };
+  // All fragments of a slice are read first, then its MFMAs run.
+  auto compute_slice = [&](const _Float16* SA, const _Float16* SB) {
+    half8 af[C::KSTEPS][C::FM], bf[C::KSTEPS][C::FN];
+    static_for<0, C::KSTEPS>([&](auto KS) {
+      const int kc = KS * 2 + (lane >> 5);
+      static_for<0, C::FM>([&](auto I) {
+        const int row = wm * C::WM + I * 32 + (lane & 31);
+        af[KS][I] = *reinterpret_cast<const half8*>(&SA[row * C::BK + ((kc ^ swz(row)) * 8)]);
+      });
+      static_for<0, C::FN>([&](auto J) {
+        const int row = wn * C::WN + J * 32 + (lane & 31);
+        bf[KS][J] = *reinterpret_cast<const half8*>(&SB[row * C::BK + ((kc ^ swz(row)) * 8)]);
+      });
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, C::KSTEPS>([&](auto KS) {
+      static_for<0, C::FM>([&](auto I) {
+        static_for<0, C::FN>([&](auto J) {
+          acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[KS][I], bf[KS][J], acc[I][J],
+                                                             0, 0, 0);
+        });
+      });
+    });
+  };
 
+  // Ring schedule: slice t+3 is requested while slice t is consumed. Before
+  // each barrier this wave waits until slice t+1 has landed; its copies of
+  // slices t+2 and t+3 may stay in flight. Requests past the last slice
+  // re-read the last slice into a stage that is never consumed again, so
+  // the loop needs no branches. K is a multiple of STAGES * BK.
+  constexpr int COPIES = BLK_A + BLK_B;
+  static_assert(2 * COPIES <= 63, "vmcnt range");
   const int nk = K / C::BK;
-  NSMI_GLOAD(0);
-  NSMI_SSTORE(0);
+  load_slice(sA0, sB0, 0);
+  load_slice(sA1, sB1, min(1, nk - 1) * C::BK);
+  load_slice(sA2, sB2, min(2, nk - 1) * C::BK);
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * COPIES));
   __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    // prefetch the next K tile (the last iteration re-reads its own tile,
-    // which keeps the loop free of branches around the loads)
-    NSMI_GLOAD(min(kt + 1, nk - 1) * C::BK);
-#pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) {
-      const int kc = ks * 2 + (lane >> 5);
-      half8 af[C::FM], bf[C::FN];
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
-        const int row = wm * C::WM + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const half8*>(&sA[cur][row * C::BK + ((kc ^ (row & 7)) * 8)]);
-      }
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        const int row = wn * C::WN + j * 32 + (lane & 31);
-        bf[j] = *reinterpret_cast<const half8*>(&sB[cur][row * C::BK + ((kc ^ (row & 7)) * 8)]);
-      }
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-    NSMI_SSTORE(cur ^ 1);
+  for (int kt = 0; kt < nk; kt += STAGES) {
+    load_slice(sA3, sB3, min(kt + 3, nk - 1) * C::BK);
+    compute_slice(sA0, sB0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * COPIES));
+    __syncthreads();
+    load_slice(sA0, sB0, min(kt + 4, nk - 1) * C::BK);
+    compute_slice(sA1, sB1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * COPIES));
+    __syncthreads();
+    load_slice(sA1, sB1, min(kt + 5, nk - 1) * C::BK);
+    compute_slice(sA2, sB2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * COPIES));
+    __syncthreads();
+    load_slice(sA2, sB2, min(kt + 6, nk - 1) * C::BK);
+    compute_slice(sA3, sB3);
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * COPIES));
     __syncthreads();
   }
-#undef NSMI_GLOAD
-#undef NSMI_SSTORE
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));   // trailing copies
+  __syncthreads();
 
   // ---------------------------------------------------------------- epilogue
-  // MFMA 32x32 output layout: register r of lane l holds row
-  // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the 32x32 block.
-  const float alpha = d.alpha, beta = d.beta, gamma = d.gamma, delta = d.delta;
-  const _Float16* Cg = d.C;
-  void* Dg = d.D;
-  _Float16* D2g = d.D2;
-  _Float16* DTg = d.DT;
-  const int ldd = d.ldd, diag_n = d.diag_n;
-  const int valid_m = d.valid_m, valid_n = d.valid_n, out_type = d.out_type;
-  const bool diag_tile = sym && (ti == tj);
-
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int col = n0 + wn * C::WN + j * 32 + (lane & 31);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int rb0 = m0 + wm * C::WM + i * 32 + g * 8 + (lane >> 5) * 4;
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = rb0 + q;
-          float x = alpha * acc[i][j][g * 4 + q];
-          if (Cg) x += beta * static_cast<float>(gmem(Cg)[static_cast<int64_t>(row) * N + col]);
-          if (row == col && row < diag_n) x += gamma;
-          v[q] = x;
-        }
-        if (sym) {
-          // lower-triangle element (row >= col) stored at (row, col) and
-          // mirrored to (col, row)
-          if (diag_tile) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int row = rb0 + q;
-              if (row < col) continue;
-              const _Float16 h = static_cast<_Float16>(v[q]);
-              gmem(static_cast<_Float16*>(Dg))[static_cast<int64_t>(row) * ldd + col] = h;
-              if (row != col) gmem(static_cast<_Float16*>(Dg))[static_cast<int64_t>(col) * ldd + row] = h;
-              if (D2g) {
-                const float y = v[q] + ((row == col && row < diag_n) ? delta : 0.f);
-                const _Float16 h2 = static_cast<_Float16>(y);
-                gmem(D2g)[static_cast<int64_t>(row) * N + col] = h2;
-                if (row != col) gmem(D2g)[static_cast<int64_t>(col) * N + row] = h2;
-              }
-            }
-          } else {
-            half4 hv;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              hv[q] = static_cast<_Float16>(v[q]);
-              gmem(static_cast<_Float16*>(Dg))[static_cast<int64_t>(rb0 + q) * ldd + col] = hv[q];
-            }
-            *gmem(reinterpret_cast<half4*>(static_cast<_Float16*>(Dg) + static_cast<int64_t>(col) * ldd + rb0)) = hv;
-            if (D2g) {
-#pragma unroll
-              for (int q = 0; q < 4; ++q) gmem(D2g)[static_cast<int64_t>(rb0 + q) * N + col] = hv[q];
-              *gmem(reinterpret_cast<half4*>(D2g + static_cast<int64_t>(col) * N + rb0)) = hv;
-            }
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int row = rb0 + q;
-            if (row < valid_m && col < valid_n)
-              store_out(Dg, out_type, static_cast<int64_t>(row) * ldd + col, v[q]);
-          }
-          if (D2g) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int row = rb0 + q;
-              const float y = v[q] + ((row == col && row < diag_n) ? delta : 0.f);
-              gmem(D2g)[static_cast<int64_t>(row) * N + col] = static_cast<_Float16>(y);
-            }
-          }
-          if (DTg) {
-            half4 hv;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) hv[q] = static_cast<_Float16>(v[q]);
-            *gmem(reinterpret_cast<half4*>(DTg + static_cast<int64_t>(col) * M + rb0)) = hv;
-          }
-        }
-      }
-    }
+  Epi e;
+  e.alpha = d.alpha; e.beta = d.beta; e.gamma = d.gamma; e.delta = d.delta;
+  e.C = d.C; e.D = d.D; e.D2 = d.D2; e.DT = d.DT;
+  e.M = M; e.N = N; e.ldd = d.ldd; e.diag_n = d.diag_n;
+  e.valid_m = d.valid_m; e.valid_n = d.valid_n; e.out_type = d.out_type;
+  e.row0 = m0 + wm * C::WM + (lane >> 5) * 4;
+  e.col0 = n0 + wn * C::WN + (lane & 31);
+  if (sym) {
+    if (ti != tj) epilogue_sym_offdiag<C>(acc, e);
+    else epilogue_sym_diag<C>(acc, e);
+  } else if (d.out_type == OUT_F16 && d.valid_m == M && d.valid_n == N) {
+    epilogue_full_f16<C>(acc, e);
+  } else {
+    epilogue_output<C>(acc, e);
   }
+#endif
 }
-
 }  // namespace
 
 int gemm_tile() { return MainCfg::BM; }
+int gemm_k_multiple() { return STAGES * MainCfg::BK; }
 
 hipError_t launch_gemm(const GemmDesc* descs, int count, int total_tiles,
                        hipStream_t stream) {

@@ -152,7 +152,21 @@ struct Stage {
   size_t off;   // byte offset of its descriptors inside the table
   int count;    // descriptors
   int total;    // workgroups (chunks / tiles)
+  double work;  // algorithmic flops (GEMM) or HBM bytes (normalisation)
 };
+
+// Problems of one grouped GEMM launch plus their algorithmic flops.
+struct Probs {
+  std::vector<GemmDesc> d;
+  double flops = 0.0;
+  void add(const GemmDesc& g, double f) {
+    d.push_back(g);
+    flops += f;
+  }
+};
+// s (s + 1) k for a symmetric product, 2 m n k for a general one.
+inline double sym_flops(int64_t s, int64_t k) { return double(s) * double(s + 1) * double(k); }
+inline double gen_flops(int64_t m, int64_t n, int64_t k) { return 2.0 * m * n * k; }
 
 struct MatBuf {   // per-matrix workspace offsets (bytes from ws base)
   int64_t m, n, s, l, Sp, Lp;
@@ -229,10 +243,11 @@ struct Builder {
   _Float16* h(size_t off) const { return reinterpret_cast<_Float16*>(ws + off); }
 
   template <class D>
-  void push(Stage::Kind kind, std::vector<D>& v, int total) {
+  void push(Stage::Kind kind, std::vector<D>& v, int total, double work) {
     if (v.empty()) return;
     Stage st;
     st.kind = kind;
+    st.work = work;
     st.off = align_up(pl.table.size(), 64);
     st.count = static_cast<int>(v.size());
     st.total = total;
@@ -243,7 +258,8 @@ struct Builder {
 
   // One grouped GEMM launch; problems ordered by tile cost (K), largest
   // first, so long tiles start early and short ones fill the tail.
-  void gemm_stage(std::vector<GemmDesc> v) {
+  void gemm_stage(Probs pr) {
+    std::vector<GemmDesc>& v = pr.d;
     std::stable_sort(v.begin(), v.end(), [](const GemmDesc& a, const GemmDesc& b) {
       if (a.K != b.K) return a.K > b.K;
       return a.tiles > b.tiles;
@@ -253,7 +269,7 @@ struct Builder {
       d.tile_begin = begin;
       begin += d.tiles;
     }
-    push(Stage::GEMM, v, begin);
+    push(Stage::GEMM, v, begin, pr.flops);
   }
 };
 
@@ -288,8 +304,12 @@ void norm_stages(Builder& B, const ns_matrix* mats, float eps) {
   Plan& pl = B.pl;
   std::vector<NormDesc> v;
   int tile_begin = 0;
+  double read_bytes = 0.0, write_bytes = 0.0;
   for (int i : pl.order) {
     const MatBuf& b = pl.mats[i];
+    const double elems = double(b.m) * double(b.n);
+    read_bytes += elems * (mats[i].g_dtype == NS_DT_F32 ? 4.0 : 2.0);
+    write_bytes += elems * 2.0 * 2.0;
     NormDesc d{};
     d.G = mats[i].g;
     d.ldg = mats[i].ldg;
@@ -323,25 +343,26 @@ void norm_stages(Builder& B, const ns_matrix* mats, float eps) {
   std::vector<NormDesc> by_chunk = v;
   std::sort(by_chunk.begin(), by_chunk.end(),
             [](const NormDesc& a, const NormDesc& b) { return a.chunk_begin < b.chunk_begin; });
-  B.push(Stage::SUMSQ, by_chunk, pl.total_chunks);
-  B.push(Stage::FINALIZE, v, static_cast<int>(v.size()));
-  B.push(Stage::CAST, v, tile_begin);
+  B.push(Stage::SUMSQ, by_chunk, pl.total_chunks, read_bytes);
+  B.push(Stage::FINALIZE, v, static_cast<int>(v.size()), 0.0);
+  B.push(Stage::CAST, v, tile_begin, read_bytes + write_bytes);
 }
 
 void final_output(Builder& B, const ns_matrix& mt, const MatBuf& b, const _Float16* Qm,
                   const _Float16* XT, const _Float16* Xc, const _Float16* XTc, float beta,
-                  std::vector<GemmDesc>& out) {
+                  Probs& out) {
   // wide: out = Q X = Q (X^T)^T                    (M = Sp, N = Lp)
   // tall: out = (Q X)^T = X^T Q^T = X^T Q (Q sym.)  (M = Lp, N = Sp)
   // (direct backend: Q is the step matrix b A + c A^2 and the epilogue adds
   //  beta times X or X^T)
   const int ot = out_code(mt.out_dtype);
+  const double f = gen_flops(b.s, b.l, b.s);
   if (!b.tall) {
-    out.push_back(gemm(Qm, XT, Xc, mt.out, nullptr, nullptr, b.Sp, b.Lp, b.Sp, mt.ldo, b.m,
-                       b.n, 0, ot, false, 1.f, beta, 0.f, 0.f));
+    out.add(gemm(Qm, XT, Xc, mt.out, nullptr, nullptr, b.Sp, b.Lp, b.Sp, mt.ldo, b.m, b.n, 0,
+                 ot, false, 1.f, beta, 0.f, 0.f), f);
   } else {
-    out.push_back(gemm(XT, Qm, XTc, mt.out, nullptr, nullptr, b.Lp, b.Sp, b.Sp, mt.ldo, b.m,
-                       b.n, 0, ot, false, 1.f, beta, 0.f, 0.f));
+    out.add(gemm(XT, Qm, XTc, mt.out, nullptr, nullptr, b.Lp, b.Sp, b.Sp, mt.ldo, b.m, b.n, 0,
+                 ot, false, 1.f, beta, 0.f, 0.f), f);
   }
 }
 
@@ -352,11 +373,12 @@ void gram_stages(Builder& B, const ns_matrix* mats, const ns_params& p) {
   for (int i = 0; i < p.num_restarts; ++i) restart[p.restarts[i]] = true;
 
   auto syrk_all = [&](int /*unused*/) {
-    std::vector<GemmDesc> v;
+    Probs v;
     for (int i : pl.order) {
       const MatBuf& b = pl.mats[i];
-      v.push_back(gemm(B.h(b.X), B.h(b.X), nullptr, B.h(b.R), nullptr, nullptr, b.Sp, b.Sp,
-                       b.Lp, b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, 0.f, 0.f, 0.f));
+      v.add(gemm(B.h(b.X), B.h(b.X), nullptr, B.h(b.R), nullptr, nullptr, b.Sp, b.Sp, b.Lp,
+                 b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, 0.f, 0.f, 0.f),
+            sym_flops(b.s, b.l));
     }
     B.gemm_stage(v);
   };
@@ -369,12 +391,12 @@ void gram_stages(Builder& B, const ns_matrix* mats, const ns_params& p) {
     const float a = p.coeffs[3 * k], bk = p.coeffs[3 * k + 1], ck = p.coeffs[3 * k + 2];
     if (restart[k] && !q_identity) {
       // restart: X <- Q X (also written transposed), R <- X X^T, Q <- I
-      std::vector<GemmDesc> v;
+      Probs v;
       for (int i : pl.order) {
         const MatBuf& b = pl.mats[i];
-        v.push_back(gemm(B.h(b.Q[qc]), B.h(b.XT[xt]), nullptr, B.h(b.X), nullptr,
-                         B.h(b.XT[xt ^ 1]), b.Sp, b.Lp, b.Sp, b.Lp, b.Sp, b.Lp, 0, OUT_F16,
-                         false, 1.f, 0.f, 0.f, 0.f));
+        v.add(gemm(B.h(b.Q[qc]), B.h(b.XT[xt]), nullptr, B.h(b.X), nullptr, B.h(b.XT[xt ^ 1]),
+                   b.Sp, b.Lp, b.Sp, b.Lp, b.Sp, b.Lp, 0, OUT_F16, false, 1.f, 0.f, 0.f, 0.f),
+              gen_flops(b.s, b.l, b.s));
       }
       B.gemm_stage(v);
       xt ^= 1;
@@ -384,27 +406,29 @@ void gram_stages(Builder& B, const ns_matrix* mats, const ns_params& p) {
     const bool need_r = (k + 1 < K) && !restart[k + 1];
     // Z = b R + c R^2 (and, right after a start or restart, Q = Z + a I)
     {
-      std::vector<GemmDesc> v;
+      Probs v;
       for (int i : pl.order) {
         const MatBuf& b = pl.mats[i];
         _Float16* q2 = q_identity ? B.h(b.Q[qc ^ 1]) : nullptr;
-        v.push_back(gemm(B.h(b.R), B.h(b.R), B.h(b.R), B.h(b.Z), q2, nullptr, b.Sp, b.Sp, b.Sp,
-                         b.Sp, b.Sp, b.Sp, b.s, OUT_F16, true, ck, bk, 0.f, a));
+        v.add(gemm(B.h(b.R), B.h(b.R), B.h(b.R), B.h(b.Z), q2, nullptr, b.Sp, b.Sp, b.Sp, b.Sp,
+                   b.Sp, b.Sp, b.s, OUT_F16, true, ck, bk, 0.f, a),
+              sym_flops(b.s, b.s));
       }
       B.gemm_stage(v);
     }
     // Q <- Z Q + a Q  and  T = Z R + a R  (both read Z; one launch)
     {
-      std::vector<GemmDesc> v;
+      Probs v;
       for (int i : pl.order) {
         const MatBuf& b = pl.mats[i];
         if (!q_identity)
-          v.push_back(gemm(B.h(b.Z), B.h(b.Q[qc]), B.h(b.Q[qc]), B.h(b.Q[qc ^ 1]), nullptr,
-                           nullptr, b.Sp, b.Sp, b.Sp, b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f,
-                           a, 0.f, 0.f));
+          v.add(gemm(B.h(b.Z), B.h(b.Q[qc]), B.h(b.Q[qc]), B.h(b.Q[qc ^ 1]), nullptr, nullptr,
+                     b.Sp, b.Sp, b.Sp, b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, a, 0.f, 0.f),
+                sym_flops(b.s, b.s));
         if (need_r)
-          v.push_back(gemm(B.h(b.Z), B.h(b.R), B.h(b.R), B.h(b.T), nullptr, nullptr, b.Sp,
-                           b.Sp, b.Sp, b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, a, 0.f, 0.f));
+          v.add(gemm(B.h(b.Z), B.h(b.R), B.h(b.R), B.h(b.T), nullptr, nullptr, b.Sp, b.Sp, b.Sp,
+                     b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, a, 0.f, 0.f),
+                sym_flops(b.s, b.s));
       }
       B.gemm_stage(v);
     }
@@ -412,16 +436,17 @@ void gram_stages(Builder& B, const ns_matrix* mats, const ns_params& p) {
     q_identity = false;
     // R <- T Z + a T   (R_{k+1} = (a I + Z) R (a I + Z))
     if (need_r) {
-      std::vector<GemmDesc> v;
+      Probs v;
       for (int i : pl.order) {
         const MatBuf& b = pl.mats[i];
-        v.push_back(gemm(B.h(b.T), B.h(b.Z), B.h(b.T), B.h(b.R), nullptr, nullptr, b.Sp, b.Sp,
-                         b.Sp, b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, a, 0.f, 0.f));
+        v.add(gemm(B.h(b.T), B.h(b.Z), B.h(b.T), B.h(b.R), nullptr, nullptr, b.Sp, b.Sp, b.Sp,
+                   b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, a, 0.f, 0.f),
+              sym_flops(b.s, b.s));
       }
       B.gemm_stage(v);
     }
   }
-  std::vector<GemmDesc> v;
+  Probs v;
   for (int i : pl.order) {
     const MatBuf& b = pl.mats[i];
     final_output(B, mats[i], b, B.h(b.Q[qc]), B.h(b.XT[xt]), nullptr, nullptr, 0.f, v);
@@ -436,20 +461,22 @@ void direct_stages(Builder& B, const ns_matrix* mats, const ns_params& p) {
   int xt = 0;
   for (int k = 0; k < K; ++k) {
     const float a = p.coeffs[3 * k], bk = p.coeffs[3 * k + 1], ck = p.coeffs[3 * k + 2];
-    std::vector<GemmDesc> v1, v2, v3;
+    Probs v1, v2, v3;
     for (int i : pl.order) {
       const MatBuf& b = pl.mats[i];
       // A = X X^T
-      v1.push_back(gemm(B.h(b.X), B.h(b.X), nullptr, B.h(b.A), nullptr, nullptr, b.Sp, b.Sp,
-                        b.Lp, b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, 0.f, 0.f, 0.f));
+      v1.add(gemm(B.h(b.X), B.h(b.X), nullptr, B.h(b.A), nullptr, nullptr, b.Sp, b.Sp, b.Lp,
+                  b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, 0.f, 0.f, 0.f),
+             sym_flops(b.s, b.l));
       // B = b A + c A^2
-      v2.push_back(gemm(B.h(b.A), B.h(b.A), B.h(b.A), B.h(b.B), nullptr, nullptr, b.Sp, b.Sp,
-                        b.Sp, b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, ck, bk, 0.f, 0.f));
+      v2.add(gemm(B.h(b.A), B.h(b.A), B.h(b.A), B.h(b.B), nullptr, nullptr, b.Sp, b.Sp, b.Sp,
+                  b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, ck, bk, 0.f, 0.f),
+             sym_flops(b.s, b.s));
       // X <- a X + B X  (in place; X^T written to the other buffer)
       if (k + 1 < K) {
-        v3.push_back(gemm(B.h(b.B), B.h(b.XT[xt]), B.h(b.X), B.h(b.X), nullptr,
-                          B.h(b.XT[xt ^ 1]), b.Sp, b.Lp, b.Sp, b.Lp, b.Sp, b.Lp, 0, OUT_F16,
-                          false, 1.f, a, 0.f, 0.f));
+        v3.add(gemm(B.h(b.B), B.h(b.XT[xt]), B.h(b.X), B.h(b.X), nullptr, B.h(b.XT[xt ^ 1]),
+                    b.Sp, b.Lp, b.Sp, b.Lp, b.Sp, b.Lp, 0, OUT_F16, false, 1.f, a, 0.f, 0.f),
+               gen_flops(b.s, b.l, b.s));
       } else {
         final_output(B, mats[i], b, B.h(b.B), B.h(b.XT[xt]), B.h(b.X), B.h(b.XT[xt]), a, v3);
       }
@@ -471,27 +498,80 @@ ns_status build_plan(Plan& pl, const ns_matrix* mats, int count, ns_backend be,
   return NS_OK;
 }
 
+// ---------------------------------------------------------------- timing
+struct TimedLaunch {
+  bool gemm;
+  double work;
+  hipEvent_t start, end;
+};
+std::mutex g_time_mu;
+bool g_timing = false;
+std::vector<TimedLaunch> g_timed;
+std::vector<hipEvent_t> g_event_pool;
+
+hipError_t take_event(hipEvent_t* ev) {
+  if (!g_event_pool.empty()) {
+    *ev = g_event_pool.back();
+    g_event_pool.pop_back();
+    return hipSuccess;
+  }
+  return hipEventCreate(ev);
+}
+
+bool timing_on() {
+  std::lock_guard<std::mutex> lock(g_time_mu);
+  return g_timing;
+}
+
+// Brackets one launch with events when timing is enabled.
+template <class F>
+hipError_t timed(bool on, bool gemm_kind, double work, hipStream_t stream, F launch) {
+  if (!on) return launch();
+  hipEvent_t a = nullptr, b = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_time_mu);
+    hipError_t e = take_event(&a);
+    if (e == hipSuccess) e = take_event(&b);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = hipEventRecord(a, stream);
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(b, stream);
+  std::lock_guard<std::mutex> lock(g_time_mu);
+  g_timed.push_back({gemm_kind, work, a, b});
+  return e;
+}
+
 ns_status run_plan(const Plan& pl, unsigned char* ws, hipStream_t stream) {
   unsigned char* table = ws + pl.table_off;
   if (upload(table, pl.table.data(), pl.table.size(), stream) != hipSuccess) return NS_ERR_HIP;
+  const bool on = timing_on();
   for (const Stage& st : pl.stages) {
     hipError_t e = hipSuccess;
     switch (st.kind) {
       case Stage::SUMSQ:
-        e = launch_sumsq(reinterpret_cast<const NormDesc*>(table + st.off), st.count, st.total,
-                         stream);
+        e = timed(on, false, st.work, stream, [&] {
+          return launch_sumsq(reinterpret_cast<const NormDesc*>(table + st.off), st.count,
+                              st.total, stream);
+        });
         break;
       case Stage::FINALIZE:
-        e = launch_norm_finalize(reinterpret_cast<const NormDesc*>(table + st.off), st.count,
-                                 stream);
+        e = timed(on, false, st.work, stream, [&] {
+          return launch_norm_finalize(reinterpret_cast<const NormDesc*>(table + st.off),
+                                      st.count, stream);
+        });
         break;
       case Stage::CAST:
-        e = launch_cast(reinterpret_cast<const NormDesc*>(table + st.off), st.count, st.total,
-                        stream);
+        e = timed(on, false, st.work, stream, [&] {
+          return launch_cast(reinterpret_cast<const NormDesc*>(table + st.off), st.count,
+                             st.total, stream);
+        });
         break;
       case Stage::GEMM:
-        e = launch_gemm(reinterpret_cast<const GemmDesc*>(table + st.off), st.count, st.total,
-                        stream);
+        e = timed(on, true, st.work, stream, [&] {
+          return launch_gemm(reinterpret_cast<const GemmDesc*>(table + st.off), st.count,
+                             st.total, stream);
+        });
         break;
     }
     if (e != hipSuccess) return NS_ERR_HIP;
@@ -566,6 +646,49 @@ NS_API const char* ns_backend_info(void) {
   std::lock_guard<std::mutex> lock(g_dev_mu);
   g_info = buf;
   return g_info.c_str();
+}
+
+NS_API ns_status ns_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lock(g_time_mu);
+  g_timing = enable != 0;
+  return NS_OK;
+}
+
+NS_API ns_status ns_timing_read(ns_timing_report* r) {
+  if (!r) return NS_ERR_INVALID_ARG;
+  std::vector<TimedLaunch> done;
+  {
+    std::lock_guard<std::mutex> lock(g_time_mu);
+    done.swap(g_timed);
+  }
+  ns_timing_report out{};
+  ns_status st = NS_OK;
+  for (const TimedLaunch& t : done) {
+    float ms = 0.f;
+    if (hipEventSynchronize(t.end) != hipSuccess ||
+        hipEventElapsedTime(&ms, t.start, t.end) != hipSuccess) {
+      st = NS_ERR_HIP;
+      ms = 0.f;
+    }
+    if (t.gemm) {
+      out.gemm_ms += ms;
+      out.gemm_launches += 1;
+      out.gemm_flops += t.work;
+    } else {
+      out.norm_ms += ms;
+      out.norm_launches += 1;
+      out.norm_bytes += t.work;
+    }
+  }
+  {
+    std::lock_guard<std::mutex> lock(g_time_mu);
+    for (const TimedLaunch& t : done) {
+      g_event_pool.push_back(t.start);
+      g_event_pool.push_back(t.end);
+    }
+  }
+  *r = out;
+  return st;
 }
 
 NS_API ns_status ns_workspace_size(const ns_matrix* mats, int count, ns_backend backend,
@@ -670,9 +793,17 @@ NS_API ns_status ns_normalize(const void* g, ns_dtype g_dtype, int64_t m, int64_
   hipStream_t st = static_cast<hipStream_t>(stream);
   NormDesc* dd = reinterpret_cast<NormDesc*>(w + np.desc_off);
   if (upload(dd, &d, sizeof(d), st) != hipSuccess) return NS_ERR_HIP;
-  if (launch_sumsq(dd, 1, np.chunks, st) != hipSuccess) return NS_ERR_HIP;
-  if (launch_norm_finalize(dd, 1, st) != hipSuccess) return NS_ERR_HIP;
-  if (launch_cast(dd, 1, d.tiles, st) != hipSuccess) return NS_ERR_HIP;
+  const bool on = timing_on();
+  const double in_bytes = double(m) * double(n) * (g_dtype == NS_DT_F32 ? 4.0 : 2.0);
+  const double out_bytes = double(m) * double(n) * 2.0;
+  if (timed(on, false, in_bytes, st, [&] { return launch_sumsq(dd, 1, np.chunks, st); }) !=
+      hipSuccess)
+    return NS_ERR_HIP;
+  if (timed(on, false, 0.0, st, [&] { return launch_norm_finalize(dd, 1, st); }) != hipSuccess)
+    return NS_ERR_HIP;
+  if (timed(on, false, in_bytes + out_bytes, st,
+            [&] { return launch_cast(dd, 1, d.tiles, st); }) != hipSuccess)
+    return NS_ERR_HIP;
   return NS_OK;
 }
 
@@ -682,7 +813,8 @@ NS_API ns_status ns_gemm_nt(const void* a, const void* b, const void* c, void* d
                             int64_t N, int64_t K, float alpha, float beta, float gamma,
                             int symmetric, void* ws, size_t ws_bytes, void* stream) {
   if (!a || !b || !d) return NS_ERR_INVALID_ARG;
-  if (M < PAD || N < PAD || K < 64 || M % PAD || N % PAD || K % 64) return NS_ERR_INVALID_ARG;
+  if (M < PAD || N < PAD || K < 1 || M % PAD || N % PAD || K % gemm_k_multiple())
+    return NS_ERR_INVALID_ARG;
   if (M > NS_MAX_DIM || N > NS_MAX_DIM || K > NS_MAX_DIM) return NS_ERR_INVALID_ARG;
   if (symmetric && M != N) return NS_ERR_INVALID_ARG;
   if (!c && beta != 0.f) return NS_ERR_INVALID_ARG;

@@ -87,7 +87,9 @@ hipError_t launch_cast(const NormDesc* descs, int count, int total_tiles,
 hipError_t launch_gemm(const GemmDesc* descs, int count, int total_tiles,
                        hipStream_t stream);
 
-// Tile edge of the GEMM kernel (BM == BN).
+// Tile edge of the GEMM kernel (BM == BN), and the multiple that every K
+// must be (the kernel's LDS ring consumes K in STAGES slices of BK).
 int gemm_tile();
+int gemm_k_multiple();
 
 }  // namespace nsmi

@@ -180,11 +180,13 @@ def test_normalize_and_unit_calls_reject_bad_arguments():
                           None) == nsmi.NS_ERR_INVALID_ARG
     assert lib.ns_gemm_nt(fake, fake, None, fake, 256, 512, 64, 1.0, 0.0, 0.0, 1, fake, ws,
                           None) == nsmi.NS_ERR_INVALID_ARG
-    assert lib.ns_gemm_nt(fake, fake, None, fake, 256, 256, 64, 1.0, 1.0, 0.0, 0, fake, ws,
+    assert lib.ns_gemm_nt(fake, fake, None, fake, 256, 256, 128, 1.0, 1.0, 0.0, 0, fake, ws,
                           None) == nsmi.NS_ERR_INVALID_ARG
-    assert lib.ns_gemm_nt(fake, fake, None, fake, 256, 256, 64, 1.0, 0.0, 0.0, 0, fake, 8,
+    assert lib.ns_gemm_nt(fake, fake, None, fake, 256, 256, 128, 1.0, 0.0, 0.0, 0, fake, 8,
                           None) == nsmi.NS_ERR_WORKSPACE
     assert lib.ns_syrk(fake, 256, 100, fake, fake, ws, None) == nsmi.NS_ERR_INVALID_ARG
+    assert lib.ns_gemm_nt(fake, fake, None, fake, 256, 256, 64, 1.0, 0.0, 0.0, 0, fake, ws,
+                          None) == nsmi.NS_ERR_INVALID_ARG
 
 
 @pytest.mark.skipif(not _no_gpu(), reason="only meaningful where no GPU is visible")
