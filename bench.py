@@ -20,8 +20,10 @@ library records around each of its launches on the caller's stream.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -47,11 +49,47 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=25.0,
                     help="seconds of oracle work for the CPU baseline sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run three plain device copies of BYTES bytes (reference "
+                         "for the FETCH_SIZE / WRITE_SIZE counters), then exit")
     return ap.parse_args()
+
+
+def calibrate_copy(nbytes):
+    """Three device-to-device copies of a known size, nothing else."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 3}), flush=True)
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+PROFILE = os.path.join(ROOT, "profiles", "gemm_nt_kernel_llama8b_owner_batch.md")
+GEMM_SRC = os.path.join(ROOT, "newton_schulz_matrix_amd", "csrc", "gemm_kernels.hip")
+
+
+def gemm_traffic_per_launch():
+    """HBM bytes per GEMM launch from the committed FETCH_SIZE / WRITE_SIZE
+    summary (default workload, gram backend), or None once the kernel source
+    differs from the one the counters were taken on."""
+    try:
+        text = open(PROFILE).read()
+        src = open(GEMM_SRC, "rb").read()
+    except OSError:
+        return None
+    m = re.search(r"gemm_nt_kernel_traffic_bytes_per_launch: ([0-9.eE+-]+)", text)
+    h = re.search(r"gemm_kernels_hip_sha256: ([0-9a-f]{64})", text)
+    if not m or not h or h.group(1) != hashlib.sha256(src).hexdigest():
+        return None
+    return float(m.group(1))
 
 
 def time_backend(nsmi, torch, Gs, outs, backend, table, restarts, steps, warmup):
@@ -142,6 +180,10 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+
     import torch
 
     import newton_schulz_matrix_amd as nsmi
@@ -209,7 +251,10 @@ def main():
         "flops_per_step": flops_step,
         "roofline": {"bound": "mfma", "kernel": "gemm_nt_kernel (grouped fp16 MFMA)",
                      "achieved": achieved, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP16_TFLOPS, "traffic": None,
+                     "frac": achieved / PEAK_FP16_TFLOPS,
+                     "traffic": (gemm_traffic_per_launch()
+                                 if args.workload == 4 and args.backend == "gram" else None),
+                     "traffic_unit": "bytes per launch (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
                      "launches_per_step": t["gemm_launches"] // K,
                      "avg_launch_ms": avg_launch_ms,
                      "flops_per_launch": flops_per_launch},
