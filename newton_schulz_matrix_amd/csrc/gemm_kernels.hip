@@ -28,8 +28,10 @@
 //   * LDS rows are 64 bytes; the 16-byte chunks are XOR-swizzled by
 //     (row / 4) % 4 so the 16 lanes served per cycle by a 128-bit LDS read
 //     (16 consecutive rows) hit 16 distinct bank groups;
-//   * per slice, all MFMA fragments are read first, then the 16 MFMAs run
-//     while the later reads are still landing;
+//   * one barrier per slice, before its MFMAs: the MFMAs of slice t run on
+//     fragments already in registers while the fragments of slice t+1 are
+//     read from LDS into a second register set (MFMA and LDS read issue
+//     interleaved one for one), so no MFMA waits on LDS latency;
 //   * workgroup ids are remapped so each XCD (8 per MI355X, one L2 each)
 //     works on runs of 32 neighbouring tiles that share operand panels.
 #include "ns_internal.h"
@@ -332,6 +334,121 @@ __device__ __forceinline__ void epilogue_output(const Acc& acc, const Epi& e) {
   });
 }
 
+// ------------------------------------------------------------------ fast epilogue
+// Row-major stores go through a per-wave LDS staging area (the operand ring
+// is idle after the main loop) so that each lane stores 16 bytes; stores of
+// the transpose use a 32-lane swap so that each lane holds 8 consecutive
+// rows of one column (16 bytes).
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  const uint16_t ua = __builtin_bit_cast(uint16_t, static_cast<_Float16>(a));
+  const uint16_t ub = __builtin_bit_cast(uint16_t, static_cast<_Float16>(b));
+  return static_cast<uint32_t>(ua) | (static_cast<uint32_t>(ub) << 16);
+}
+__device__ __forceinline__ float lo_h(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
+}
+__device__ __forceinline__ float hi_h(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+// After lane_swap(x, y): lanes 32..63 of x hold lanes 0..31 of the old y and
+// lanes 0..31 of y hold lanes 32..63 of the old x (v_permlane32_swap).
+__device__ __forceinline__ void lane_swap(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  x = r[0];
+  y = r[1];
+}
+
+// Staging layout: 128 x 64 fp16 per wave, row-major, 16-byte chunks of rows
+// 4..7 (mod 8) XOR-ed by 4 so the two row groups written by one instruction
+// (rows r and r+4) fall on different banks.
+__device__ __forceinline__ int stage_idx(int row, int col) {
+  return row * 64 + ((((col >> 3) ^ (((row >> 2) & 1) << 2))) << 3) + (col & 7);
+}
+
+template <class Cf, bool SYM_C, bool HAS_C_FULL, class Acc>
+__device__ __forceinline__ void epilogue_staged(const Acc& acc, const Epi& e, _Float16* W,
+                                                int lane, int wrow0, int wcol0,
+                                                _Float16* T, int ldT, _Float16* T2) {
+  static_assert(Cf::WM == 128 && Cf::WN == 64, "staging area is 128 x 64 per wave");
+  const int h = lane >> 5;
+  static_for<0, Cf::FM>([&](auto I) {
+    static_for<0, Cf::FN>([&](auto J) {
+      const floatx16& a = acc[I][J];
+      const int col = wcol0 + J * 32 + (lane & 31);          // global column
+      const int rbase = wrow0 + I * 32;                        // global row of block
+      uint32_t P[4][2];
+      static_for<0, 2>([&](auto GP) {                          // register group pairs
+        constexpr int g0 = 2 * GP;
+        float c[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        if constexpr (SYM_C) {
+          if (e.C) {
+            // C symmetric: C[r][col] == C[col][r]; 8 consecutive rows in one load
+            const u32x4 cv = *gmem(reinterpret_cast<const u32x4*>(
+                e.C + static_cast<int64_t>(col) * e.N + rbase + 8 * (g0 + h)));
+            uint32_t x0 = cv[0], x1 = cv[1], y0 = cv[2], y1 = cv[3];
+            lane_swap(x0, y0);
+            lane_swap(x1, y1);
+            c[0][0] = lo_h(x0); c[0][1] = hi_h(x0); c[0][2] = lo_h(x1); c[0][3] = hi_h(x1);
+            c[1][0] = lo_h(y0); c[1][1] = hi_h(y0); c[1][2] = lo_h(y1); c[1][3] = hi_h(y1);
+          }
+        }
+        static_for<0, 2>([&](auto GG) {
+          constexpr int g = g0 + GG;
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row = rbase + g * 8 + h * 4 + q;
+            float x = e.alpha * a[g * 4 + q];
+            if constexpr (SYM_C) x += e.beta * c[GG][q];
+            if constexpr (HAS_C_FULL)
+              x += e.beta * static_cast<float>(gmem(e.C)[static_cast<int64_t>(row) * e.N + col]);
+            if (row == col && col < e.diag_n) x += e.gamma;
+            v[q] = x;
+          }
+          P[g][0] = pack_h2(v[0], v[1]);
+          P[g][1] = pack_h2(v[2], v[3]);
+          // row-major staging (local coordinates inside the wave's 128 x 64)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int lr = I * 32 + g * 8 + h * 4 + q, lc = J * 32 + (lane & 31);
+            const uint32_t w = P[g][q >> 1];
+            W[stage_idx(lr, lc)] =
+                __builtin_bit_cast(_Float16, static_cast<uint16_t>((q & 1) ? (w >> 16) : (w & 0xffffu)));
+          }
+        });
+      });
+      // transposed copy: 8 consecutive rows per lane after the swap
+      if (T) {
+        static_for<0, 2>([&](auto GP) {
+          constexpr int g0 = 2 * GP;
+          uint32_t x0 = P[g0][0], x1 = P[g0][1], y0 = P[g0 + 1][0], y1 = P[g0 + 1][1];
+          lane_swap(x0, y0);
+          lane_swap(x1, y1);
+          const u32x4 out = {x0, x1, y0, y1};
+          const int64_t off = static_cast<int64_t>(col) * ldT + rbase + 8 * (g0 + h);
+          *gmem(reinterpret_cast<u32x4*>(T + off)) = out;
+          if (T2) *gmem(reinterpret_cast<u32x4*>(T2 + off)) = out;
+        });
+      }
+    });
+  });
+  // row-major copy out of the staging area: 16 bytes per lane, 8 lanes per row
+  _Float16* D = static_cast<_Float16*>(e.D);
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int id = it * 64 + lane;
+    const int lr = id >> 3, ch = id & 7;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(&W[stage_idx(lr, ch * 8)]);
+    const int64_t off = static_cast<int64_t>(wrow0 + lr) * e.ldd + wcol0 + ch * 8;
+    *gmem(reinterpret_cast<u32x4*>(D + off)) = val;
+    if (e.D2) *gmem(reinterpret_cast<u32x4*>(e.D2 + static_cast<int64_t>(wrow0 + lr) * e.N +
+                                             wcol0 + ch * 8)) = val;
+  }
+}
+
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
     const GemmDesc* __restrict__ descs, int count, int total_tiles) {
@@ -395,61 +512,76 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
     });
     __builtin_amdgcn_sched_barrier(0);   // keep the copies at the top
   };
-  // All fragments of a slice are read first, then its MFMAs run.
-  auto compute_slice = [&](const _Float16* SA, const _Float16* SB) {
-    half8 af[C::KSTEPS][C::FM], bf[C::KSTEPS][C::FN];
+  constexpr int COPIES = BLK_A + BLK_B;
+  static_assert(3 * COPIES <= 63, "vmcnt range");
+  // Fragment register sets: the MFMAs of slice t run on one set while the
+  // fragments of slice t+1 are read into the other.
+  half8 fa0[C::KSTEPS][C::FM], fb0[C::KSTEPS][C::FN];
+  half8 fa1[C::KSTEPS][C::FM], fb1[C::KSTEPS][C::FN];
+  auto read_frags = [&](const _Float16* SA, const _Float16* SB, auto& fa, auto& fb) {
     static_for<0, C::KSTEPS>([&](auto KS) {
       const int kc = KS * 2 + (lane >> 5);
       static_for<0, C::FM>([&](auto I) {
         const int row = wm * C::WM + I * 32 + (lane & 31);
-        af[KS][I] = *reinterpret_cast<const half8*>(&SA[row * C::BK + ((kc ^ swz(row)) * 8)]);
+        fa[KS][I] = *reinterpret_cast<const half8*>(&SA[row * C::BK + ((kc ^ swz(row)) * 8)]);
       });
       static_for<0, C::FN>([&](auto J) {
         const int row = wn * C::WN + J * 32 + (lane & 31);
-        bf[KS][J] = *reinterpret_cast<const half8*>(&SB[row * C::BK + ((kc ^ swz(row)) * 8)]);
+        fb[KS][J] = *reinterpret_cast<const half8*>(&SB[row * C::BK + ((kc ^ swz(row)) * 8)]);
       });
     });
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto mfmas = [&](auto& fa, auto& fb) {
     static_for<0, C::KSTEPS>([&](auto KS) {
       static_for<0, C::FM>([&](auto I) {
         static_for<0, C::FN>([&](auto J) {
-          acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[KS][I], bf[KS][J], acc[I][J],
+          acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[KS][I], fb[KS][J], acc[I][J],
                                                              0, 0, 0);
         });
       });
     });
   };
+  constexpr int NREAD = C::KSTEPS * (C::FM + C::FN);
+  constexpr int NMFMA = C::KSTEPS * C::FM * C::FN;
+  static_assert(NMFMA >= NREAD, "interleave pattern");
+  // One iteration: wait until slice t+1 has landed everywhere (which also
+  // means every wave is done reading slice t's stage), refill slice t's
+  // stage with slice t+4, then run the MFMAs of slice t interleaved with
+  // the fragment reads of slice t+1.
+  auto step = [&](_Float16* SAt, _Float16* SBt, const _Float16* SAn, const _Float16* SBn,
+                  auto& fac, auto& fbc, auto& fan, auto& fbn, int k_next4) {
+    // also lgkmcnt(0): this wave's reads of slice t's stage must be complete
+    // before the barrier after which that stage is refilled
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * COPIES) & ~0x0F00);
+    __syncthreads();
+    load_slice(SAt, SBt, k_next4);
+    read_frags(SAn, SBn, fan, fbn);
+    mfmas(fac, fbc);
+    static_for<0, NREAD>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    });
+    __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  // Ring schedule: slice t+3 is requested while slice t is consumed. Before
-  // each barrier this wave waits until slice t+1 has landed; its copies of
-  // slices t+2 and t+3 may stay in flight. Requests past the last slice
-  // re-read the last slice into a stage that is never consumed again, so
-  // the loop needs no branches. K is a multiple of STAGES * BK.
-  constexpr int COPIES = BLK_A + BLK_B;
-  static_assert(2 * COPIES <= 63, "vmcnt range");
+  // Ring schedule: slices t+2..t+4 in flight while slice t is multiplied.
+  // K is a multiple of STAGES * BK; requests past the last slice re-read the
+  // last slice into a stage that is never consumed again.
   const int nk = K / C::BK;
+  auto kclamp = [&](int sl) { return min(sl, nk - 1) * C::BK; };
   load_slice(sA0, sB0, 0);
-  load_slice(sA1, sB1, min(1, nk - 1) * C::BK);
-  load_slice(sA2, sB2, min(2, nk - 1) * C::BK);
-  __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * COPIES));
+  load_slice(sA1, sB1, kclamp(1));
+  load_slice(sA2, sB2, kclamp(2));
+  load_slice(sA3, sB3, kclamp(3));
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * COPIES));
   __syncthreads();
+  read_frags(sA0, sB0, fa0, fb0);
   for (int kt = 0; kt < nk; kt += STAGES) {
-    load_slice(sA3, sB3, min(kt + 3, nk - 1) * C::BK);
-    compute_slice(sA0, sB0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * COPIES));
-    __syncthreads();
-    load_slice(sA0, sB0, min(kt + 4, nk - 1) * C::BK);
-    compute_slice(sA1, sB1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * COPIES));
-    __syncthreads();
-    load_slice(sA1, sB1, min(kt + 5, nk - 1) * C::BK);
-    compute_slice(sA2, sB2);
-    __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * COPIES));
-    __syncthreads();
-    load_slice(sA2, sB2, min(kt + 6, nk - 1) * C::BK);
-    compute_slice(sA3, sB3);
-    __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * COPIES));
-    __syncthreads();
+    step(sA0, sB0, sA1, sB1, fa0, fb0, fa1, fb1, kclamp(kt + 4));
+    step(sA1, sB1, sA2, sB2, fa1, fb1, fa0, fb0, kclamp(kt + 5));
+    step(sA2, sB2, sA3, sB3, fa0, fb0, fa1, fb1, kclamp(kt + 6));
+    step(sA3, sB3, sA0, sB0, fa1, fb1, fa0, fb0, kclamp(kt + 7));
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));   // trailing copies
   __syncthreads();
@@ -462,11 +594,29 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   e.valid_m = d.valid_m; e.valid_n = d.valid_n; e.out_type = d.out_type;
   e.row0 = m0 + wm * C::WM + (lane >> 5) * 4;
   e.col0 = n0 + wn * C::WN + (lane & 31);
+  // The operand ring is reused as per-wave staging for the fast paths; all
+  // waves must be done with it (and with their last fragment reads).
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0) & ~0x0F00);
+  __syncthreads();
+  // wave w stages into the w-th 16 KB array of the ring
+  _Float16* W = wave == 0 ? sA0 : wave == 1 ? sB0 : wave == 2 ? sA1 : wave == 3 ? sB1
+              : wave == 4 ? sA2 : wave == 5 ? sB2 : wave == 6 ? sA3 : sB3;
+  const int wrow0 = m0 + wm * C::WM, wcol0 = n0 + wn * C::WN;
+  const bool row_store_ok =
+      (d.ldd % 8 == 0) && (reinterpret_cast<uintptr_t>(d.D) % 16 == 0);
   if (sym) {
-    if (ti != tj) epilogue_sym_offdiag<C>(acc, e);
-    else epilogue_sym_diag<C>(acc, e);
-  } else if (d.out_type == OUT_F16 && d.valid_m == M && d.valid_n == N) {
-    epilogue_full_f16<C>(acc, e);
+    if (ti != tj) {
+      epilogue_staged<C, true, false>(acc, e, W, lane, wrow0, wcol0,
+                                      static_cast<_Float16*>(d.D), d.ldd, d.D2);
+    } else {
+      epilogue_sym_diag<C>(acc, e);
+    }
+  } else if (d.out_type == OUT_F16 && d.valid_m == M && d.valid_n == N && row_store_ok &&
+             !d.D2) {
+    if (d.C)
+      epilogue_staged<C, false, true>(acc, e, W, lane, wrow0, wcol0, d.DT, M, nullptr);
+    else
+      epilogue_staged<C, false, false>(acc, e, W, lane, wrow0, wcol0, d.DT, M, nullptr);
   } else {
     epilogue_output<C>(acc, e);
   }
