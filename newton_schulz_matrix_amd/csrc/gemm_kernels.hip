@@ -30,8 +30,10 @@
 //     (16 consecutive rows) hit 16 distinct bank groups;
 //   * one barrier per slice, before its MFMAs: the MFMAs of slice t run on
 //     fragments already in registers while the fragments of slice t+1 are
-//     read from LDS into a second register set (MFMA and LDS read issue
-//     interleaved one for one), so no MFMA waits on LDS latency;
+//     read from LDS into a second register set; each step is issued in four
+//     quarters of (one copy of slice t+4, three fragment reads, four
+//     MFMAs), so copies, LDS reads and MFMAs overlap instead of bursting
+//     after the barrier;
 //   * workgroup ids are remapped so each XCD (8 per MI355X, one L2 each)
 //     works on runs of 32 neighbouring tiles that share operand panels.
 #include "ns_internal.h"
@@ -548,21 +550,45 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   // means every wave is done reading slice t's stage), refill slice t's
   // stage with slice t+4, then run the MFMAs of slice t interleaved with
   // the fragment reads of slice t+1.
+  // One step in four quarters: each quarter issues one of this wave's four
+  // copies (slice t+4), three fragment reads of slice t+1 and four MFMAs of
+  // slice t, so copies, reads and MFMAs are spread over the whole step.
+  static_assert(BLK_A == 2 && BLK_B == 2 && NREAD == 12 && NMFMA == 16, "quarter plan");
   auto step = [&](_Float16* SAt, _Float16* SBt, const _Float16* SAn, const _Float16* SBn,
                   auto& fac, auto& fbc, auto& fan, auto& fbn, int k_next4) {
-    // also lgkmcnt(0): this wave's reads of slice t's stage must be complete
-    // before the barrier after which that stage is refilled
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * COPIES) & ~0x0F00);
     __syncthreads();
-    load_slice(SAt, SBt, k_next4);
-    read_frags(SAn, SBn, fan, fbn);
-    mfmas(fac, fbc);
-    static_for<0, NREAD>([&](auto) {
+    const uint32_t kb = static_cast<uint32_t>(k_next4) * 2u;
+    __builtin_amdgcn_s_setprio(1);   // this wave's MFMA/copy stream first
+    static_for<0, 4>([&](auto Q) {
+      if constexpr (Q < 2) lds_copy16(rA, lds_addr_of(SAt + (wv * BLK_A + Q) * 512), a_off[Q], kb);
+      else lds_copy16(rB, lds_addr_of(SBt + (wv * BLK_B + (Q - 2)) * 512), b_off[Q - 2], kb);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, 3>([&](auto R) {
+        constexpr int idx = Q * 3 + R;            // 0..11, KS-major: A0..A3, B0, B1
+        constexpr int KS = idx / 6, w = idx % 6;
+        const int kc = KS * 2 + (lane >> 5);
+        if constexpr (w < 4) {
+          const int row = wm * C::WM + w * 32 + (lane & 31);
+          fan[KS][w] = *reinterpret_cast<const half8*>(&SAn[row * C::BK + ((kc ^ swz(row)) * 8)]);
+        } else {
+          const int row = wn * C::WN + (w - 4) * 32 + (lane & 31);
+          fbn[KS][w - 4] = *reinterpret_cast<const half8*>(&SBn[row * C::BK + ((kc ^ swz(row)) * 8)]);
+        }
+      });
+      static_for<0, 4>([&](auto R) {
+        constexpr int idx = Q * 4 + R;            // 0..15, KS-major, then I, J
+        constexpr int KS = idx / 8, I = (idx % 8) / 2, J = idx % 2;
+        acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fac[KS][I], fbc[KS][J], acc[I][J], 0, 0, 0);
+      });
+      static_for<0, 3>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      });
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
     });
-    __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Ring schedule: slices t+2..t+4 in flight while slice t is multiplied.
