@@ -219,104 +219,9 @@ __device__ __forceinline__ void epi_values(const floatx16& a, const Epi& e, int 
   }
 }
 
-// Symmetric product, tile strictly below the diagonal: store (i, j) and
-// the mirror (j, i) of every element; no diagonal terms occur.
-template <class Cf, class Acc>
-__device__ __forceinline__ void epilogue_sym_offdiag(const Acc& acc, const Epi& e) {
-  _Float16* D = static_cast<_Float16*>(e.D);
-  static_for<0, Cf::FM>([&](auto I) {
-    static_for<0, Cf::FN>([&](auto J) {
-      const floatx16& a = acc[I][J];
-      static_for<0, 4>([&](auto G) {
-        int rb, col;
-        block_coords<Cf, I, J, G>(e, rb, col);
-        float v[4];
-        epi_values<G>(a, e, rb, col, v);
-        half4 hv;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          hv[q] = static_cast<_Float16>(v[q]);
-          gmem(D)[static_cast<int64_t>(rb + q) * e.ldd + col] = hv[q];
-        }
-        *gmem(reinterpret_cast<half4*>(D + static_cast<int64_t>(col) * e.ldd + rb)) = hv;
-        if (e.D2) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) gmem(e.D2)[static_cast<int64_t>(rb + q) * e.N + col] = hv[q];
-          *gmem(reinterpret_cast<half4*>(e.D2 + static_cast<int64_t>(col) * e.N + rb)) = hv;
-        }
-      });
-    });
-  });
-}
-
-// Symmetric product, diagonal tile: elements on or below the diagonal are
-// stored at (i, j) and mirrored; the upper half is never taken from acc.
-template <class Cf, class Acc>
-__device__ __forceinline__ void epilogue_sym_diag(const Acc& acc, const Epi& e) {
-  _Float16* D = static_cast<_Float16*>(e.D);
-  static_for<0, Cf::FM>([&](auto I) {
-    static_for<0, Cf::FN>([&](auto J) {
-      const floatx16& a = acc[I][J];
-      static_for<0, 4>([&](auto G) {
-        int rb, col;
-        block_coords<Cf, I, J, G>(e, rb, col);
-        float v[4];
-        epi_values<G>(a, e, rb, col, v);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = rb + q;
-          if (row < col) continue;
-          const _Float16 h = static_cast<_Float16>(v[q]);
-          gmem(D)[static_cast<int64_t>(row) * e.ldd + col] = h;
-          if (row != col) gmem(D)[static_cast<int64_t>(col) * e.ldd + row] = h;
-          if (e.D2) {
-            const float y = v[q] + ((row == col && row < e.diag_n) ? e.delta : 0.f);
-            const _Float16 h2 = static_cast<_Float16>(y);
-            gmem(e.D2)[static_cast<int64_t>(row) * e.N + col] = h2;
-            if (row != col) gmem(e.D2)[static_cast<int64_t>(col) * e.N + row] = h2;
-          }
-        }
-      });
-    });
-  });
-}
-
-// General product into an internal fp16 buffer, optionally also written
-// transposed (DT, leading dimension M).
-template <class Cf, class Acc>
-__device__ __forceinline__ void epilogue_full_f16(const Acc& acc, const Epi& e) {
-  _Float16* D = static_cast<_Float16*>(e.D);
-  static_for<0, Cf::FM>([&](auto I) {
-    static_for<0, Cf::FN>([&](auto J) {
-      const floatx16& a = acc[I][J];
-      static_for<0, 4>([&](auto G) {
-        int rb, col;
-        block_coords<Cf, I, J, G>(e, rb, col);
-        float v[4];
-        epi_values<G>(a, e, rb, col, v);
-        half4 hv;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          hv[q] = static_cast<_Float16>(v[q]);
-          gmem(D)[static_cast<int64_t>(rb + q) * e.ldd + col] = hv[q];
-        }
-        if (e.D2) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int row = rb + q;
-            const float y = v[q] + ((row == col && row < e.diag_n) ? e.delta : 0.f);
-            gmem(e.D2)[static_cast<int64_t>(row) * e.N + col] = static_cast<_Float16>(y);
-          }
-        }
-        if (e.DT)
-          *gmem(reinterpret_cast<half4*>(e.DT + static_cast<int64_t>(col) * e.M + rb)) = hv;
-      });
-    });
-  });
-}
-
-// Final output: user buffer, dtype fp16 / bf16 / fp32, clipped to the real
-// (valid_m, valid_n) block.
+// Scalar epilogue for general products whose output is not an fp16 internal
+// buffer: user buffer, dtype fp16 / bf16 / fp32, clipped to the real
+// (valid_m, valid_n) block (no second output).
 template <class Cf, class Acc>
 __device__ __forceinline__ void epilogue_output(const Acc& acc, const Epi& e) {
   static_for<0, Cf::FM>([&](auto I) {
@@ -363,31 +268,46 @@ __device__ __forceinline__ void lane_swap(uint32_t& x, uint32_t& y) {
   y = r[1];
 }
 
-// Staging layout: 128 x 64 fp16 per wave, row-major, 16-byte chunks of rows
-// 4..7 (mod 8) XOR-ed by 4 so the two row groups written by one instruction
-// (rows r and r+4) fall on different banks.
-__device__ __forceinline__ int stage_idx(int row, int col) {
-  return row * 64 + ((((col >> 3) ^ (((row >> 2) & 1) << 2))) << 3) + (col & 7);
+// Output staging: the whole 256 x 256 fp16 tile, row-major, 16-byte chunks
+// XOR-swizzled by f(row) = 8 (row & 1) + 4 ((row >> 2) & 1): the two rows a
+// register store covers (r and r+4) and the two rows 16 lanes read back
+// (r and r+1) fall on different banks.
+__device__ __forceinline__ int tile_idx(int row, int col) {
+  const int f = ((row & 1) << 3) | (((row >> 2) & 1) << 2);
+  return row * 256 + ((((col >> 3) ^ f)) << 3) + (col & 7);
 }
 
-template <class Cf, bool SYM_C, bool HAS_C_FULL, class Acc>
-__device__ __forceinline__ void epilogue_staged(const Acc& acc, const Epi& e, _Float16* W,
-                                                int lane, int wrow0, int wcol0,
-                                                _Float16* T, int ldT, _Float16* T2) {
-  static_assert(Cf::WM == 128 && Cf::WN == 64, "staging area is 128 x 64 per wave");
+enum EpiMode { EPI_SYM_OFFDIAG, EPI_SYM_DIAG, EPI_FULL, EPI_FULL_C };
+
+// Fast epilogue for fp16 outputs inside internal (padded, aligned) buffers:
+//   * v = alpha acc + beta C + gamma (real diagonal) in fp32, rounded once;
+//   * row-major stores staged through LDS, 16 bytes per lane;
+//   * transposed stores (symmetric mirror, or DT) from registers after a
+//     32-lane swap, 16 bytes per lane;
+//   * symmetric C read from its transpose in 16-byte chunks;
+//   * diagonal tiles: elements on/below the diagonal are staged at (r, c)
+//     and (c, r), so the tile comes out exactly symmetric; the second output
+//     D2 = D + delta I takes delta on the fp32 diagonal value.
+template <class Cf, int MODE, class Acc>
+__device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Float16* S,
+                                              float* sdiag, int lane, int wm, int wn,
+                                              int m0, int n0, _Float16* T, int ldT,
+                                              _Float16* T2) {
+  static_assert(Cf::BM == 256 && Cf::BN == 256, "tile-wide staging is 256 x 256");
+  constexpr bool SYM = MODE == EPI_SYM_OFFDIAG || MODE == EPI_SYM_DIAG;
   const int h = lane >> 5;
   static_for<0, Cf::FM>([&](auto I) {
     static_for<0, Cf::FN>([&](auto J) {
       const floatx16& a = acc[I][J];
-      const int col = wcol0 + J * 32 + (lane & 31);          // global column
-      const int rbase = wrow0 + I * 32;                        // global row of block
+      const int lcol = wn * Cf::WN + J * 32 + (lane & 31);     // tile-local column
+      const int lrow0 = wm * Cf::WM + I * 32;                   // tile-local block row
+      const int col = n0 + lcol, rbase = m0 + lrow0;            // global
       uint32_t P[4][2];
-      static_for<0, 2>([&](auto GP) {                          // register group pairs
+      static_for<0, 2>([&](auto GP) {
         constexpr int g0 = 2 * GP;
         float c[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        if constexpr (SYM_C) {
+        if constexpr (SYM) {
           if (e.C) {
-            // C symmetric: C[r][col] == C[col][r]; 8 consecutive rows in one load
             const u32x4 cv = *gmem(reinterpret_cast<const u32x4*>(
                 e.C + static_cast<int64_t>(col) * e.N + rbase + 8 * (g0 + h)));
             uint32_t x0 = cv[0], x1 = cv[1], y0 = cv[2], y1 = cv[3];
@@ -404,50 +324,72 @@ __device__ __forceinline__ void epilogue_staged(const Acc& acc, const Epi& e, _F
           for (int q = 0; q < 4; ++q) {
             const int row = rbase + g * 8 + h * 4 + q;
             float x = e.alpha * a[g * 4 + q];
-            if constexpr (SYM_C) x += e.beta * c[GG][q];
-            if constexpr (HAS_C_FULL)
+            if constexpr (SYM) x += e.beta * c[GG][q];
+            if constexpr (MODE == EPI_FULL_C)
               x += e.beta * static_cast<float>(gmem(e.C)[static_cast<int64_t>(row) * e.N + col]);
             if (row == col && col < e.diag_n) x += e.gamma;
             v[q] = x;
           }
           P[g][0] = pack_h2(v[0], v[1]);
           P[g][1] = pack_h2(v[2], v[3]);
-          // row-major staging (local coordinates inside the wave's 128 x 64)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int lr = I * 32 + g * 8 + h * 4 + q, lc = J * 32 + (lane & 31);
+            const int lr = lrow0 + g * 8 + h * 4 + q;
             const uint32_t w = P[g][q >> 1];
-            W[stage_idx(lr, lc)] =
+            const _Float16 hv =
                 __builtin_bit_cast(_Float16, static_cast<uint16_t>((q & 1) ? (w >> 16) : (w & 0xffffu)));
+            if constexpr (MODE == EPI_SYM_DIAG) {
+              if (lr >= lcol) {
+                S[tile_idx(lr, lcol)] = hv;
+                if (lr != lcol) S[tile_idx(lcol, lr)] = hv;
+                else sdiag[lr] = v[q];
+              }
+            } else {
+              S[tile_idx(lr, lcol)] = hv;
+            }
           }
         });
       });
-      // transposed copy: 8 consecutive rows per lane after the swap
-      if (T) {
-        static_for<0, 2>([&](auto GP) {
-          constexpr int g0 = 2 * GP;
-          uint32_t x0 = P[g0][0], x1 = P[g0][1], y0 = P[g0 + 1][0], y1 = P[g0 + 1][1];
-          lane_swap(x0, y0);
-          lane_swap(x1, y1);
-          const u32x4 out = {x0, x1, y0, y1};
-          const int64_t off = static_cast<int64_t>(col) * ldT + rbase + 8 * (g0 + h);
-          *gmem(reinterpret_cast<u32x4*>(T + off)) = out;
-          if (T2) *gmem(reinterpret_cast<u32x4*>(T2 + off)) = out;
-        });
+      if constexpr (MODE != EPI_SYM_DIAG) {
+        if (T) {   // transposed copy: 8 consecutive rows per lane after the swap
+          static_for<0, 2>([&](auto GP) {
+            constexpr int g0 = 2 * GP;
+            uint32_t x0 = P[g0][0], x1 = P[g0][1], y0 = P[g0 + 1][0], y1 = P[g0 + 1][1];
+            lane_swap(x0, y0);
+            lane_swap(x1, y1);
+            const u32x4 out = {x0, x1, y0, y1};
+            const int64_t off = static_cast<int64_t>(col) * ldT + rbase + 8 * (g0 + h);
+            *gmem(reinterpret_cast<u32x4*>(T + off)) = out;
+            if (T2) *gmem(reinterpret_cast<u32x4*>(T2 + off)) = out;
+          });
+        }
       }
     });
   });
-  // row-major copy out of the staging area: 16 bytes per lane, 8 lanes per row
+  // Diagonal tiles mirror across waves: wait for every wave's staging.
+  if constexpr (MODE == EPI_SYM_DIAG) __syncthreads();
+  // Row-major copy of this wave's 128 x 64 block: 16 bytes per lane.
   _Float16* D = static_cast<_Float16*>(e.D);
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
     const int id = it * 64 + lane;
-    const int lr = id >> 3, ch = id & 7;
-    const u32x4 val = *reinterpret_cast<const u32x4*>(&W[stage_idx(lr, ch * 8)]);
-    const int64_t off = static_cast<int64_t>(wrow0 + lr) * e.ldd + wcol0 + ch * 8;
+    const int lr = wm * Cf::WM + (id >> 3), lc = wn * Cf::WN + (id & 7) * 8;
+    u32x4 val = *reinterpret_cast<const u32x4*>(&S[tile_idx(lr, lc)]);
+    const int64_t off = static_cast<int64_t>(m0 + lr) * e.ldd + n0 + lc;
     *gmem(reinterpret_cast<u32x4*>(D + off)) = val;
-    if (e.D2) *gmem(reinterpret_cast<u32x4*>(e.D2 + static_cast<int64_t>(wrow0 + lr) * e.N +
-                                             wcol0 + ch * 8)) = val;
+    if (e.D2) {
+      if constexpr (MODE == EPI_SYM_DIAG) {
+        // the second output adds delta on the real diagonal, from fp32
+        if (lr >= lc && lr < lc + 8 && m0 + lr < e.diag_n) {
+          const int k = lr - lc;
+          const uint16_t hb = __builtin_bit_cast(uint16_t, static_cast<_Float16>(sdiag[lr] + e.delta));
+          const uint32_t w = val[k >> 1];
+          val[k >> 1] = (k & 1) ? ((w & 0xffffu) | (static_cast<uint32_t>(hb) << 16))
+                                : ((w & 0xffff0000u) | hb);
+        }
+      }
+      *gmem(reinterpret_cast<u32x4*>(e.D2 + static_cast<int64_t>(m0 + lr) * e.N + n0 + lc)) = val;
+    }
   }
 }
 
@@ -456,10 +398,19 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
     const GemmDesc* __restrict__ descs, int count, int total_tiles) {
 #if defined(__HIP_DEVICE_COMPILE__)
   // Four stages as distinct LDS objects (the loop below is unrolled by four).
-  __shared__ __attribute__((aligned(1024))) _Float16 sA0[C::A_ELEMS], sB0[C::B_ELEMS];
-  __shared__ __attribute__((aligned(1024))) _Float16 sA1[C::A_ELEMS], sB1[C::B_ELEMS];
-  __shared__ __attribute__((aligned(1024))) _Float16 sA2[C::A_ELEMS], sB2[C::B_ELEMS];
-  __shared__ __attribute__((aligned(1024))) _Float16 sA3[C::A_ELEMS], sB3[C::B_ELEMS];
+  // One LDS block: during the K loop, four stages of (A slice, B slice);
+  // in the epilogue, the 256 x 256 fp16 output tile (same 128 KB).
+  static_assert(STAGES * (C::A_ELEMS + C::B_ELEMS) == C::BM * C::BN, "LDS reuse");
+  __shared__ __attribute__((aligned(1024))) _Float16 smem[STAGES * (C::A_ELEMS + C::B_ELEMS)];
+  __shared__ float sdiag[C::BM];   // fp32 diagonal of a diagonal tile (second output)
+  _Float16* const sA0 = smem;
+  _Float16* const sB0 = smem + 1 * C::A_ELEMS;
+  _Float16* const sA1 = smem + 2 * C::A_ELEMS;
+  _Float16* const sB1 = smem + 3 * C::A_ELEMS;
+  _Float16* const sA2 = smem + 4 * C::A_ELEMS;
+  _Float16* const sB2 = smem + 5 * C::A_ELEMS;
+  _Float16* const sA3 = smem + 6 * C::A_ELEMS;
+  _Float16* const sB3 = smem + 7 * C::A_ELEMS;
 
   const int t_logical = xcd_remap(blockIdx.x, total_tiles);
   const int p = find_problem(descs, count, t_logical);
@@ -620,29 +571,25 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   e.valid_m = d.valid_m; e.valid_n = d.valid_n; e.out_type = d.out_type;
   e.row0 = m0 + wm * C::WM + (lane >> 5) * 4;
   e.col0 = n0 + wn * C::WN + (lane & 31);
-  // The operand ring is reused as per-wave staging for the fast paths; all
-  // waves must be done with it (and with their last fragment reads).
+  // The operand ring is reused as the output staging tile; all waves must
+  // be done with it (and with their last fragment reads and copies).
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0) & ~0x0F00);
   __syncthreads();
-  // wave w stages into the w-th 16 KB array of the ring
-  _Float16* W = wave == 0 ? sA0 : wave == 1 ? sB0 : wave == 2 ? sA1 : wave == 3 ? sB1
-              : wave == 4 ? sA2 : wave == 5 ? sB2 : wave == 6 ? sA3 : sB3;
-  const int wrow0 = m0 + wm * C::WM, wcol0 = n0 + wn * C::WN;
   const bool row_store_ok =
       (d.ldd % 8 == 0) && (reinterpret_cast<uintptr_t>(d.D) % 16 == 0);
   if (sym) {
-    if (ti != tj) {
-      epilogue_staged<C, true, false>(acc, e, W, lane, wrow0, wcol0,
-                                      static_cast<_Float16*>(d.D), d.ldd, d.D2);
-    } else {
-      epilogue_sym_diag<C>(acc, e);
-    }
+    if (ti != tj)
+      epilogue_tile<C, EPI_SYM_OFFDIAG>(acc, e, smem, sdiag, lane, wm, wn, m0, n0,
+                                        static_cast<_Float16*>(d.D), d.ldd, d.D2);
+    else
+      epilogue_tile<C, EPI_SYM_DIAG>(acc, e, smem, sdiag, lane, wm, wn, m0, n0, nullptr, 0,
+                                     nullptr);
   } else if (d.out_type == OUT_F16 && d.valid_m == M && d.valid_n == N && row_store_ok &&
              !d.D2) {
     if (d.C)
-      epilogue_staged<C, false, true>(acc, e, W, lane, wrow0, wcol0, d.DT, M, nullptr);
+      epilogue_tile<C, EPI_FULL_C>(acc, e, smem, sdiag, lane, wm, wn, m0, n0, d.DT, M, nullptr);
     else
-      epilogue_staged<C, false, false>(acc, e, W, lane, wrow0, wcol0, d.DT, M, nullptr);
+      epilogue_tile<C, EPI_FULL>(acc, e, smem, sdiag, lane, wm, wn, m0, n0, d.DT, M, nullptr);
   } else {
     epilogue_output<C>(acc, e);
   }
