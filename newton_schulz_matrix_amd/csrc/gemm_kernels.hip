@@ -76,10 +76,12 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // Buffer descriptor (gfx9 layout): 48-bit base, stride 0, size in bytes;
 // reads past `bytes` return zero.
 __device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
+  // every word is wave-uniform; readfirstlane keeps the descriptor in SGPRs,
+  // which the copy instruction requires
   const uint64_t a = reinterpret_cast<uint64_t>(p);
-  i32x4 r = {static_cast<int>(static_cast<uint32_t>(a)),
-             static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffff),
-             static_cast<int>(bytes), 0x00020000};
+  i32x4 r = {__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a))),
+             __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffff)),
+             __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)), 0x00020000};
   return r;
 }
 
@@ -131,13 +133,36 @@ __device__ __forceinline__ void decode_full(int t, int tiles_m, int tiles_n,
   tj = rem / rows;
 }
 
-// Logical tile of a symmetric problem -> (ti, tj), tj <= ti, row by row.
-__device__ __forceinline__ void decode_lower(int t, int& ti, int& tj) {
-  int r = static_cast<int>((sqrtf(8.f * t + 1.f) - 1.f) * 0.5f);
-  while ((r + 1) * (r + 2) / 2 <= t) ++r;
-  while (r * (r + 1) / 2 > t) --r;
-  ti = r;
-  tj = t - r * (r + 1) / 2;
+// Logical tile of a symmetric problem -> (ti, tj), tj <= ti: the lower
+// triangle of the T x T tile grid cut into bands of 4 tile rows, each band
+// walked column by column (like full problems), so 32 consecutive tiles span
+// about 4 A panels and 8 B panels. A full band b starts at 8b^2 + 2b.
+__device__ __forceinline__ void decode_lower(int t, int T, int& ti, int& tj) {
+  constexpr int BAND = 4;
+  int b = 0, start = 0;
+  for (;;) {                                   // at most T / 4 iterations
+    const int rows = min(BAND, T - BAND * b);
+    const int size = (BAND * b + 1) * rows + rows * (rows - 1) / 2;
+    if (t < start + size || rows <= 0) break;
+    start += size;
+    ++b;
+  }
+  const int rows = min(BAND, T - BAND * b);
+  int r = t - start;
+  const int first = (BAND * b + 1) * rows;    // columns 0 .. 4b hold `rows` tiles each
+  if (r < first) {
+    tj = r / rows;
+    ti = BAND * b + r % rows;
+    return;
+  }
+  r -= first;
+  int u = 1;                                   // column 4b + u holds rows - u tiles
+  while (r >= rows - u) {
+    r -= rows - u;
+    ++u;
+  }
+  tj = BAND * b + u;
+  ti = BAND * b + u + r;
 }
 
 __device__ __forceinline__ int find_problem(const GemmDesc* descs, int count, int t) {
@@ -419,7 +444,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   const int M = d.M, N = d.N, K = d.K;
   const bool sym = d.symmetric != 0;
   int ti, tj;
-  if (sym) decode_lower(t, ti, tj);
+  if (sym) decode_lower(t, d.tiles_n, ti, tj);
   else decode_full(t, M / C::BM, d.tiles_n, ti, tj);
   const int m0 = ti * C::BM, n0 = tj * C::BN;
 
