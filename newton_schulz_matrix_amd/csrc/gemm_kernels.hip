@@ -452,6 +452,15 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
+  // beta * C taken from the B slices (C == B^T): global row i of C is
+  // column k = i of B, so this wave's 32-row block I arrives with K slice
+  // m0 / BK + wm * FM + I. With WM == STAGES * BK that slice sits in ring
+  // position I of ring round m0 / (STAGES * BK) + wm.
+  static_assert(C::FM == STAGES && C::WM == STAGES * C::BK, "fold: one ring round per wave");
+  const bool fold = d.c_is_bt != 0;
+  const float rho = fold ? d.beta / d.alpha : 0.f;
+  const int fold_round = fold ? m0 / (STAGES * C::BK) + wm : -1;
+
   floatx16 acc[C::FM][C::FN];
   static_for<0, C::FM>([&](auto I) {
     static_for<0, C::FN>([&](auto J) {
@@ -519,6 +528,20 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
       });
     });
   };
+  // acc[I][J] += rho * C for the 32 rows of block I, read from slice SB:
+  // lane l needs rows 8g + 4(l/32) .. +3 (g = 0..3) of column l%32 of block
+  // J, i.e. four consecutive k of B row (block J column), 8 bytes.
+  auto fold_c = [&](const _Float16* SB, auto I) {
+    static_for<0, C::FN>([&](auto J) {
+      const int row = wn * C::WN + J * 32 + (lane & 31);
+      const _Float16* base = SB + row * C::BK + 4 * (lane >> 5);
+      static_for<0, 4>([&](auto G) {
+        const half4 c = *reinterpret_cast<const half4*>(base + ((G ^ swz(row)) * 8));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[I][J][G * 4 + q] += rho * static_cast<float>(c[q]);
+      });
+    });
+  };
   constexpr int NREAD = C::KSTEPS * (C::FM + C::FN);
   constexpr int NMFMA = C::KSTEPS * C::FM * C::FN;
   static_assert(NMFMA >= NREAD, "interleave pattern");
@@ -530,10 +553,15 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   // copies (slice t+4), three fragment reads of slice t+1 and four MFMAs of
   // slice t, so copies, reads and MFMAs are spread over the whole step.
   static_assert(BLK_A == 2 && BLK_B == 2 && NREAD == 12 && NMFMA == 16, "quarter plan");
-  auto step = [&](_Float16* SAt, _Float16* SBt, const _Float16* SAn, const _Float16* SBn,
-                  auto& fac, auto& fbc, auto& fan, auto& fbn, int k_next4) {
+  // The step at ring position P also folds C from slice t+1 (position
+  // (P+1) % 4, ring round `round_next`) when that slice holds this wave's rows.
+  auto step = [&](auto P, _Float16* SAt, _Float16* SBt, const _Float16* SAn,
+                  const _Float16* SBn, auto& fac, auto& fbc, auto& fan, auto& fbn, int k_next4,
+                  int round_next) {
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * COPIES) & ~0x0F00);
     __syncthreads();
+    if (round_next == fold_round) fold_c(SBn, std::integral_constant<int, (P + 1) % STAGES>{});
+    __builtin_amdgcn_sched_barrier(0);
     const uint32_t kb = static_cast<uint32_t>(k_next4) * 2u;
     __builtin_amdgcn_s_setprio(1);   // this wave's MFMA/copy stream first
     static_for<0, 4>([&](auto Q) {
@@ -579,11 +607,17 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * COPIES));
   __syncthreads();
   read_frags(sA0, sB0, fa0, fb0);
+  if (fold_round == 0) fold_c(sB0, std::integral_constant<int, 0>{});
   for (int kt = 0; kt < nk; kt += STAGES) {
-    step(sA0, sB0, sA1, sB1, fa0, fb0, fa1, fb1, kclamp(kt + 4));
-    step(sA1, sB1, sA2, sB2, fa1, fb1, fa0, fb0, kclamp(kt + 5));
-    step(sA2, sB2, sA3, sB3, fa0, fb0, fa1, fb1, kclamp(kt + 6));
-    step(sA3, sB3, sA0, sB0, fa1, fb1, fa0, fb0, kclamp(kt + 7));
+    const int round = kt / STAGES;
+    step(std::integral_constant<int, 0>{}, sA0, sB0, sA1, sB1, fa0, fb0, fa1, fb1,
+         kclamp(kt + 4), round);
+    step(std::integral_constant<int, 1>{}, sA1, sB1, sA2, sB2, fa1, fb1, fa0, fb0,
+         kclamp(kt + 5), round);
+    step(std::integral_constant<int, 2>{}, sA2, sB2, sA3, sB3, fa0, fb0, fa1, fb1,
+         kclamp(kt + 6), round);
+    step(std::integral_constant<int, 3>{}, sA3, sB3, sA0, sB0, fa1, fb1, fa0, fb0,
+         kclamp(kt + 7), round + 1);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));   // trailing copies
   __syncthreads();
@@ -591,7 +625,8 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   // ---------------------------------------------------------------- epilogue
   Epi e;
   e.alpha = d.alpha; e.beta = d.beta; e.gamma = d.gamma; e.delta = d.delta;
-  e.C = d.C; e.D = d.D; e.D2 = d.D2; e.DT = d.DT;
+  e.C = fold ? nullptr : d.C;   // folded C is already in the accumulators
+  e.D = d.D; e.D2 = d.D2; e.DT = d.DT;
   e.M = M; e.N = N; e.ldd = d.ldd; e.diag_n = d.diag_n;
   e.valid_m = d.valid_m; e.valid_n = d.valid_n; e.out_type = d.out_type;
   e.row0 = m0 + wm * C::WM + (lane >> 5) * 4;
@@ -611,7 +646,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
                                      nullptr);
   } else if (d.out_type == OUT_F16 && d.valid_m == M && d.valid_n == N && row_store_ok &&
              !d.D2) {
-    if (d.C)
+    if (e.C)
       epilogue_tile<C, EPI_FULL_C>(acc, e, smem, sdiag, lane, wm, wn, m0, n0, d.DT, M, nullptr);
     else
       epilogue_tile<C, EPI_FULL>(acc, e, smem, sdiag, lane, wm, wn, m0, n0, d.DT, M, nullptr);

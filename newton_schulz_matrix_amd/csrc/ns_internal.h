@@ -23,6 +23,9 @@ enum OutType : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 //   D2[i][j] = v + (i == j && i < diag_n ? delta : 0)      (fp16, ld N)
 //   DT[j][i] = v                       (fp16, transposed, leading dim M)
 // Stores to D are clipped to i < valid_m, j < valid_n.
+// If c_is_bt: the caller guarantees C[i][j] == B[j][i] (C is B^T, which
+// needs M <= K), alpha != 0, and the kernel takes beta * C from the B
+// slices already in LDS during the K loop instead of reading C again.
 // If symmetric: M == N, only tiles on or below the diagonal are computed
 // and every stored element (i, j), i >= j, is also stored at (j, i) in D
 // and D2, so both come out exactly symmetric.
@@ -39,6 +42,7 @@ struct GemmDesc {
   int diag_n;
   int out_type;
   int symmetric;
+  int c_is_bt;
   int tile_begin;      // first logical tile of this problem in the launch
   int tiles;           // number of tiles of this problem
   int tiles_n;         // full: N / BN ; symmetric: M / BM
