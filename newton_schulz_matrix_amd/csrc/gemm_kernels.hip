@@ -20,20 +20,22 @@
 // the direct-space step X <- a X + (b A + c A^2) X (section "直接空间 NS").
 //
 // Kernel structure (gfx950):
-//   * 256 x 256 workgroup tile, 8 waves (two per SIMD), each owning a
-//     128 x 64 sub-tile of 32x32x16 fp16 MFMAs with fp32 accumulators;
+//   * 256 x 256 workgroup tile, 8 waves in two groups of four (one wave of
+//     each group per SIMD); each wave owns a 128 x 64 sub-tile of 32x32x16
+//     fp16 MFMAs with fp32 accumulators;
 //   * operand tiles move global -> LDS by the buffer-load-to-LDS path (no
-//     register staging), through a four-stage ring of 256 x 32 slices so
-//     that the slice three steps ahead is in flight while one is consumed;
+//     register staging), through a four-stage ring of 256 x 32 slices;
+//     group 0 copies the A slices, group 1 the B slices;
+//   * ping-pong schedule: in each phase one group issues its 16 MFMAs back
+//     to back while the other group reads the next slice's fragments and
+//     issues its copies, with one barrier per phase, so the MFMA pipe of
+//     every SIMD is fed by one wave while the other waits on memory;
+//   * internal matrices use the row-pair layout (see ns_internal.h): a
+//     32-column slice of 16 rows is 8 whole 128-byte lines, which the copy
+//     path moves about 1.5x faster than 16 half lines of a row-major matrix;
 //   * LDS rows are 64 bytes; the 16-byte chunks are XOR-swizzled by
 //     (row / 4) % 4 so the 16 lanes served per cycle by a 128-bit LDS read
 //     (16 consecutive rows) hit 16 distinct bank groups;
-//   * one barrier per slice, before its MFMAs: the MFMAs of slice t run on
-//     fragments already in registers while the fragments of slice t+1 are
-//     read from LDS into a second register set; each step is issued in four
-//     quarters of (one copy of slice t+4, three fragment reads, four
-//     MFMAs), so copies, LDS reads and MFMAs overlap instead of bursting
-//     after the barrier;
 //   * workgroup ids are remapped so each XCD (8 per MI355X, one L2 each)
 //     works on runs of 32 neighbouring tiles that share operand panels.
 #include "ns_internal.h"
@@ -219,8 +221,15 @@ struct Epi {
   _Float16* D2;
   _Float16* DT;
   int M, N, ldd, diag_n, valid_m, valid_n, out_type;
+  int c_pairs, d_pairs;   // row-pair layout of C / of D, D2, DT
   int row0, col0;   // this lane's first row / column inside the tile
 };
+
+// Element (i, j) of a matrix with leading dimension ld, row-major or in the
+// row-pair layout.
+__device__ __forceinline__ int64_t lidx(int pairs, int64_t i, int64_t j, int64_t ld) {
+  return pairs ? pair_index(i, j, ld) : i * ld + j;
+}
 
 // MFMA 32x32 output layout: register r of lane l holds row
 // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of each 32x32 block. For block
@@ -238,7 +247,7 @@ __device__ __forceinline__ void epi_values(const floatx16& a, const Epi& e, int 
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     float x = e.alpha * a[G * 4 + q];
-    if (e.C) x += e.beta * static_cast<float>(gmem(e.C)[static_cast<int64_t>(rb + q) * e.N + col]);
+    if (e.C) x += e.beta * static_cast<float>(gmem(e.C)[lidx(e.c_pairs, rb + q, col, e.N)]);
     if (rb + q == col && col < e.diag_n) x += e.gamma;
     v[q] = x;
   }
@@ -260,7 +269,7 @@ __device__ __forceinline__ void epilogue_output(const Acc& acc, const Epi& e) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (rb + q < e.valid_m && col < e.valid_n)
-            store_out(e.D, e.out_type, static_cast<int64_t>(rb + q) * e.ldd + col, v[q]);
+            store_out(e.D, e.out_type, lidx(e.d_pairs, rb + q, col, e.ldd), v[q]);
       });
     });
   });
@@ -334,7 +343,7 @@ __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Flo
         if constexpr (SYM) {
           if (e.C) {
             const u32x4 cv = *gmem(reinterpret_cast<const u32x4*>(
-                e.C + static_cast<int64_t>(col) * e.N + rbase + 8 * (g0 + h)));
+                e.C + lidx(e.c_pairs, col, rbase + 8 * (g0 + h), e.N)));
             uint32_t x0 = cv[0], x1 = cv[1], y0 = cv[2], y1 = cv[3];
             lane_swap(x0, y0);
             lane_swap(x1, y1);
@@ -351,7 +360,7 @@ __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Flo
             float x = e.alpha * a[g * 4 + q];
             if constexpr (SYM) x += e.beta * c[GG][q];
             if constexpr (MODE == EPI_FULL_C)
-              x += e.beta * static_cast<float>(gmem(e.C)[static_cast<int64_t>(row) * e.N + col]);
+              x += e.beta * static_cast<float>(gmem(e.C)[lidx(e.c_pairs, row, col, e.N)]);
             if (row == col && col < e.diag_n) x += e.gamma;
             v[q] = x;
           }
@@ -383,7 +392,7 @@ __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Flo
             lane_swap(x0, y0);
             lane_swap(x1, y1);
             const u32x4 out = {x0, x1, y0, y1};
-            const int64_t off = static_cast<int64_t>(col) * ldT + rbase + 8 * (g0 + h);
+            const int64_t off = lidx(e.d_pairs, col, rbase + 8 * (g0 + h), ldT);
             *gmem(reinterpret_cast<u32x4*>(T + off)) = out;
             if (T2) *gmem(reinterpret_cast<u32x4*>(T2 + off)) = out;
           });
@@ -400,7 +409,7 @@ __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Flo
     const int id = it * 64 + lane;
     const int lr = wm * Cf::WM + (id >> 3), lc = wn * Cf::WN + (id & 7) * 8;
     u32x4 val = *reinterpret_cast<const u32x4*>(&S[tile_idx(lr, lc)]);
-    const int64_t off = static_cast<int64_t>(m0 + lr) * e.ldd + n0 + lc;
+    const int64_t off = lidx(e.d_pairs, m0 + lr, n0 + lc, e.ldd);
     *gmem(reinterpret_cast<u32x4*>(D + off)) = val;
     if (e.D2) {
       if constexpr (MODE == EPI_SYM_DIAG) {
@@ -413,7 +422,7 @@ __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Flo
                                 : ((w & 0xffff0000u) | hb);
         }
       }
-      *gmem(reinterpret_cast<u32x4*>(e.D2 + static_cast<int64_t>(m0 + lr) * e.N + n0 + lc)) = val;
+      *gmem(reinterpret_cast<u32x4*>(e.D2 + lidx(e.d_pairs, m0 + lr, n0 + lc, e.N))) = val;
     }
   }
 }
@@ -428,14 +437,8 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   static_assert(STAGES * (C::A_ELEMS + C::B_ELEMS) == C::BM * C::BN, "LDS reuse");
   __shared__ __attribute__((aligned(1024))) _Float16 smem[STAGES * (C::A_ELEMS + C::B_ELEMS)];
   __shared__ float sdiag[C::BM];   // fp32 diagonal of a diagonal tile (second output)
-  _Float16* const sA0 = smem;
-  _Float16* const sB0 = smem + 1 * C::A_ELEMS;
-  _Float16* const sA1 = smem + 2 * C::A_ELEMS;
-  _Float16* const sB1 = smem + 3 * C::A_ELEMS;
-  _Float16* const sA2 = smem + 4 * C::A_ELEMS;
-  _Float16* const sB2 = smem + 5 * C::A_ELEMS;
-  _Float16* const sA3 = smem + 6 * C::A_ELEMS;
-  _Float16* const sB3 = smem + 7 * C::A_ELEMS;
+  auto stA = [&](int s) { return smem + s * (C::A_ELEMS + C::B_ELEMS); };
+  auto stB = [&](int s) { return smem + s * (C::A_ELEMS + C::B_ELEMS) + C::A_ELEMS; };
 
   const int t_logical = xcd_remap(blockIdx.x, total_tiles);
   const int p = find_problem(descs, count, t_logical);
@@ -449,7 +452,8 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   const int m0 = ti * C::BM, n0 = tj * C::BN;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
   // beta * C taken from the B slices (C == B^T): global row i of C is
@@ -469,38 +473,38 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
     });
   });
 
-  // Copies: each wave instruction fills 1 KB of LDS = 16 tile rows of 64
-  // bytes; lane l lands on row l/4, physical chunk l%4, so it fetches
-  // logical chunk (l%4) ^ swz(row) of that row. Offsets are relative to the
-  // tile's row panel; the K position goes in the scalar offset.
-  constexpr int NW = C::THREADS / 64;
-  constexpr int RPB = 1024 / (C::BK * 2);
-  constexpr int BLK_A = C::BM / RPB / NW, BLK_B = C::BN / RPB / NW;
+  // Copies. The four waves of group 0 (tile rows 0-127) copy every A slice
+  // and the four of group 1 every B slice. Each wave instruction fills 1 KB
+  // of LDS = 16 tile rows of 64 bytes; lane l lands on row l/4, physical
+  // chunk l%4, so it fetches logical chunk (l%4) ^ swz(row) of that row.
+  // Offsets are relative to the tile's row panel; the K position goes in
+  // the scalar offset: 2 bytes per column of a row-major operand, 4 in the
+  // row-pair layout (a 32-column block of two rows is 128 bytes).
+  constexpr int RPB = 1024 / (C::BK * 2);          // rows per copy instruction
+  constexpr int COPIES = C::BM / RPB / C::WAVES_N; // per wave and slice
+  static_assert(C::WAVES_M == 2 && COPIES == 4, "ping-pong plan: two groups of four waves");
+  const int grp = wm, gw = wn;
+  const bool my_pairs = (grp == 0 ? d.a_pairs : d.b_pairs) != 0;
   const uint32_t panel_bytes = static_cast<uint32_t>(C::BM) * K * 2u;
-  const i32x4 rA = make_rsrc(d.A + static_cast<int64_t>(m0) * K, panel_bytes);
-  const i32x4 rB = make_rsrc(d.B + static_cast<int64_t>(n0) * K, panel_bytes);
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t a_off[BLK_A], b_off[BLK_B];
-  static_for<0, BLK_A>([&](auto i) {
-    const int row = (wv * BLK_A + i) * RPB + lane / C::KCH;
-    a_off[i] = (static_cast<uint32_t>(row) * K + (((lane % C::KCH) ^ swz(row)) * 8)) * 2u;
+  const i32x4 rMy = grp == 0 ? make_rsrc(d.A + static_cast<int64_t>(m0) * K, panel_bytes)
+                             : make_rsrc(d.B + static_cast<int64_t>(n0) * K, panel_bytes);
+  const uint32_t kbytes = my_pairs ? 4u : 2u;
+  uint32_t my_off[COPIES];
+  static_for<0, COPIES>([&](auto i) {
+    const int row = (gw * COPIES + i) * RPB + lane / C::KCH;
+    const int col = ((lane % C::KCH) ^ swz(row)) * 8;
+    my_off[i] = static_cast<uint32_t>(my_pairs ? (row >> 1) * 2 * K + (row & 1) * 32 + col
+                                               : row * K + col) * 2u;
   });
-  static_for<0, BLK_B>([&](auto i) {
-    const int row = (wv * BLK_B + i) * RPB + lane / C::KCH;
-    b_off[i] = (static_cast<uint32_t>(row) * K + (((lane % C::KCH) ^ swz(row)) * 8)) * 2u;
-  });
-  auto load_slice = [&](_Float16* SA, _Float16* SB, int k0) {
-    const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
-    static_for<0, BLK_A>([&](auto i) {
-      lds_copy16(rA, lds_addr_of(SA + (wv * BLK_A + i) * 512), a_off[i], kb);
+  // this wave's share of slice k0 of its group's operand into ring stage s
+  auto copy_my = [&](int s, int k0) {
+    const uint32_t kb = static_cast<uint32_t>(k0) * kbytes;
+    _Float16* base = (grp == 0 ? stA(s) : stB(s)) + gw * COPIES * 512;
+    static_for<0, COPIES>([&](auto i) {
+      lds_copy16(rMy, lds_addr_of(base + i * 512), my_off[i], kb);
     });
-    static_for<0, BLK_B>([&](auto i) {
-      lds_copy16(rB, lds_addr_of(SB + (wv * BLK_B + i) * 512), b_off[i], kb);
-    });
-    __builtin_amdgcn_sched_barrier(0);   // keep the copies at the top
+    __builtin_amdgcn_sched_barrier(0);
   };
-  constexpr int COPIES = BLK_A + BLK_B;
-  static_assert(3 * COPIES <= 63, "vmcnt range");
   // Fragment register sets: the MFMAs of slice t run on one set while the
   // fragments of slice t+1 are read into the other.
   half8 fa0[C::KSTEPS][C::FM], fb0[C::KSTEPS][C::FN];
@@ -542,85 +546,71 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
       });
     });
   };
-  constexpr int NREAD = C::KSTEPS * (C::FM + C::FN);
-  constexpr int NMFMA = C::KSTEPS * C::FM * C::FN;
-  static_assert(NMFMA >= NREAD, "interleave pattern");
-  // One iteration: wait until slice t+1 has landed everywhere (which also
-  // means every wave is done reading slice t's stage), refill slice t's
-  // stage with slice t+4, then run the MFMAs of slice t interleaved with
-  // the fragment reads of slice t+1.
-  // One step in four quarters: each quarter issues one of this wave's four
-  // copies (slice t+4), three fragment reads of slice t+1 and four MFMAs of
-  // slice t, so copies, reads and MFMAs are spread over the whole step.
-  static_assert(BLK_A == 2 && BLK_B == 2 && NREAD == 12 && NMFMA == 16, "quarter plan");
-  // The step at ring position P also folds C from slice t+1 (position
-  // (P+1) % 4, ring round `round_next`) when that slice holds this wave's rows.
-  auto step = [&](auto P, _Float16* SAt, _Float16* SBt, const _Float16* SAn,
-                  const _Float16* SBn, auto& fac, auto& fbc, auto& fan, auto& fbn, int k_next4,
-                  int round_next) {
+  // Ping-pong schedule, one barrier per phase. On every SIMD one wave of
+  // each group is resident; in each phase one group streams MFMAs from
+  // registers while the other feeds LDS:
+  //   phase 2t:   group 0 multiplies slice t; group 1 copies its half of
+  //               slice t+3 into the stage of slice t-1 (read by both groups
+  //               by now) and reads the fragments of slice t;
+  //   phase 2t+1: group 1 multiplies slice t; group 0 copies its half of
+  //               slice t+4 into the stage of slice t and reads slice t+1.
+  // Before each barrier a wave waits for its LDS reads and for its own
+  // copies of the slice read next (at most two later slices, 8 copies,
+  // stay in flight), so a slice is complete in LDS before anyone reads it.
+  auto phase_end = [&]() {
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * COPIES) & ~0x0F00);
-    __syncthreads();
-    if (round_next == fold_round) fold_c(SBn, std::integral_constant<int, (P + 1) % STAGES>{});
+    __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    const uint32_t kb = static_cast<uint32_t>(k_next4) * 2u;
-    __builtin_amdgcn_s_setprio(1);   // this wave's MFMA/copy stream first
-    static_for<0, 4>([&](auto Q) {
-      if constexpr (Q < 2) lds_copy16(rA, lds_addr_of(SAt + (wv * BLK_A + Q) * 512), a_off[Q], kb);
-      else lds_copy16(rB, lds_addr_of(SBt + (wv * BLK_B + (Q - 2)) * 512), b_off[Q - 2], kb);
-      __builtin_amdgcn_sched_barrier(0);
-      static_for<0, 3>([&](auto R) {
-        constexpr int idx = Q * 3 + R;            // 0..11, KS-major: A0..A3, B0, B1
-        constexpr int KS = idx / 6, w = idx % 6;
-        const int kc = KS * 2 + (lane >> 5);
-        if constexpr (w < 4) {
-          const int row = wm * C::WM + w * 32 + (lane & 31);
-          fan[KS][w] = *reinterpret_cast<const half8*>(&SAn[row * C::BK + ((kc ^ swz(row)) * 8)]);
-        } else {
-          const int row = wn * C::WN + (w - 4) * 32 + (lane & 31);
-          fbn[KS][w - 4] = *reinterpret_cast<const half8*>(&SBn[row * C::BK + ((kc ^ swz(row)) * 8)]);
-        }
-      });
-      static_for<0, 4>([&](auto R) {
-        constexpr int idx = Q * 4 + R;            // 0..15, KS-major, then I, J
-        constexpr int KS = idx / 8, I = (idx % 8) / 2, J = idx % 2;
-        acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fac[KS][I], fbc[KS][J], acc[I][J], 0, 0, 0);
-      });
-      static_for<0, 3>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      });
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    __builtin_amdgcn_s_setprio(0);
   };
-
-  // Ring schedule: slices t+2..t+4 in flight while slice t is multiplied.
+  auto mfma_phase = [&](auto& fa, auto& fb) {
+    mfmas(fa, fb);
+    __builtin_amdgcn_sched_barrier(0);
+  };
   // K is a multiple of STAGES * BK; requests past the last slice re-read the
   // last slice into a stage that is never consumed again.
   const int nk = K / C::BK;
   auto kclamp = [&](int sl) { return min(sl, nk - 1) * C::BK; };
-  load_slice(sA0, sB0, 0);
-  load_slice(sA1, sB1, kclamp(1));
-  load_slice(sA2, sB2, kclamp(2));
-  load_slice(sA3, sB3, kclamp(3));
-  __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * COPIES));
-  __syncthreads();
-  read_frags(sA0, sB0, fa0, fb0);
-  if (fold_round == 0) fold_c(sB0, std::integral_constant<int, 0>{});
-  for (int kt = 0; kt < nk; kt += STAGES) {
-    const int round = kt / STAGES;
-    step(std::integral_constant<int, 0>{}, sA0, sB0, sA1, sB1, fa0, fb0, fa1, fb1,
-         kclamp(kt + 4), round);
-    step(std::integral_constant<int, 1>{}, sA1, sB1, sA2, sB2, fa1, fb1, fa0, fb0,
-         kclamp(kt + 5), round);
-    step(std::integral_constant<int, 2>{}, sA2, sB2, sA3, sB3, fa0, fb0, fa1, fb1,
-         kclamp(kt + 6), round);
-    step(std::integral_constant<int, 3>{}, sA3, sB3, sA0, sB0, fa1, fb1, fa0, fb0,
-         kclamp(kt + 7), round + 1);
+  static_for<0, STAGES>([&](auto s) { copy_my(s, kclamp(s)); });
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0) & ~0x0F00);
+  __builtin_amdgcn_s_barrier();
+  if (grp == 0) {
+    read_frags(stA(0), stB(0), fa0, fb0);
+    if (fold_round == 0) fold_c(stB(0), std::integral_constant<int, 0>{});
+    phase_end();
+    for (int kt = 0; kt < nk; kt += STAGES) {
+      static_for<0, STAGES>([&](auto U) {
+        constexpr int u = U;
+        auto& fa = (u % 2 == 0) ? fa0 : fa1;
+        auto& fb = (u % 2 == 0) ? fb0 : fb1;
+        auto& fan = (u % 2 == 0) ? fa1 : fa0;
+        auto& fbn = (u % 2 == 0) ? fb1 : fb0;
+        mfma_phase(fa, fb);
+        phase_end();
+        copy_my(u, kclamp(kt + u + 4));
+        read_frags(stA((u + 1) % STAGES), stB((u + 1) % STAGES), fan, fbn);
+        if (kt / STAGES + (u == STAGES - 1 ? 1 : 0) == fold_round)
+          fold_c(stB((u + 1) % STAGES), std::integral_constant<int, (u + 1) % STAGES>{});
+        phase_end();
+      });
+    }
+  } else {
+    phase_end();
+    for (int kt = 0; kt < nk; kt += STAGES) {
+      static_for<0, STAGES>([&](auto U) {
+        constexpr int u = U;
+        auto& fa = (u % 2 == 0) ? fa0 : fa1;
+        auto& fb = (u % 2 == 0) ? fb0 : fb1;
+        if (kt + u >= 1) copy_my((u + 3) % STAGES, kclamp(kt + u + 3));
+        read_frags(stA(u), stB(u), fa, fb);
+        if (kt / STAGES == fold_round) fold_c(stB(u), std::integral_constant<int, u>{});
+        phase_end();
+        mfma_phase(fa, fb);
+        phase_end();
+      });
+    }
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));   // trailing copies
-  __syncthreads();
+  __builtin_amdgcn_s_barrier();
 
   // ---------------------------------------------------------------- epilogue
   Epi e;
@@ -629,6 +619,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   e.D = d.D; e.D2 = d.D2; e.DT = d.DT;
   e.M = M; e.N = N; e.ldd = d.ldd; e.diag_n = d.diag_n;
   e.valid_m = d.valid_m; e.valid_n = d.valid_n; e.out_type = d.out_type;
+  e.c_pairs = d.c_pairs; e.d_pairs = d.d_pairs;
   e.row0 = m0 + wm * C::WM + (lane >> 5) * 4;
   e.col0 = n0 + wn * C::WN + (lane & 31);
   // The operand ring is reused as the output staging tile; all waves must

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void cast_kernel(const NormDesc* __restrict__ 
       tile[li][c8 + e] = h[e];
     }
     if (d.P && i < d.pm) {
-      _Float16* dst = d.P + static_cast<int64_t>(i) * d.ldp + j;
+      _Float16* dst = d.P + (d.pairs ? pair_index(i, j, d.ldp) : static_cast<int64_t>(i) * d.ldp + j);
       if (j + 8 <= d.pn && (reinterpret_cast<uintptr_t>(dst) % 16 == 0)) {
         uint4 w;
         __builtin_memcpy(&w, h, 16);
@@ -187,7 +187,8 @@ __global__ __launch_bounds__(256) void cast_kernel(const NormDesc* __restrict__ 
     _Float16 h[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[e] = tile[c8 + e][lj];
-    _Float16* dst = d.PT + static_cast<int64_t>(jrow) * d.ldpt + icol;
+    _Float16* dst =
+        d.PT + (d.pairs ? pair_index(jrow, icol, d.ldpt) : static_cast<int64_t>(jrow) * d.ldpt + icol);
     if (icol + 8 <= d.pm && (reinterpret_cast<uintptr_t>(dst) % 16 == 0)) {
       uint4 w;
       __builtin_memcpy(&w, h, 16);

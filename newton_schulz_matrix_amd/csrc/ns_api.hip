@@ -156,10 +156,15 @@ struct Stage {
 };
 
 // Problems of one grouped GEMM launch plus their algorithmic flops.
+// Products of one grouped launch. Every operand of the iteration lives in
+// the workspace in the row-pair layout; so does every output except the
+// final one, which goes to the caller's row-major buffer.
 struct Probs {
   std::vector<GemmDesc> d;
   double flops = 0.0;
-  void add(const GemmDesc& g, double f) {
+  void add(GemmDesc g, double f, bool user_output = false) {
+    g.a_pairs = g.b_pairs = g.c_pairs = 1;
+    g.d_pairs = user_output ? 0 : 1;
     d.push_back(g);
     flops += f;
   }
@@ -335,6 +340,7 @@ void norm_stages(Builder& B, const ns_matrix* mats, float eps) {
       d.PT = B.h(b.X); d.ldpt = b.Lp;
     }
     d.eps = eps;
+    d.pairs = 1;
     d.norm_out = nullptr;
     d.norm_slot = reinterpret_cast<float*>(B.ws + pl.norms_off) + i;
     d.partials = reinterpret_cast<float*>(B.ws + pl.partials_off);
@@ -368,10 +374,10 @@ void final_output(Builder& B, const ns_matrix& mt, const MatBuf& b, const _Float
   const double f = gen_flops(b.s, b.l, b.s);
   if (!b.tall) {
     out.add(c_from_b(gemm(Qm, XT, Xc, mt.out, nullptr, nullptr, b.Sp, b.Lp, b.Sp, mt.ldo, b.m,
-                          b.n, 0, ot, false, 1.f, beta, 0.f, 0.f)), f);
+                          b.n, 0, ot, false, 1.f, beta, 0.f, 0.f)), f, true);
   } else {
     out.add(gemm(XT, Qm, XTc, mt.out, nullptr, nullptr, b.Lp, b.Sp, b.Sp, mt.ldo, b.m, b.n, 0,
-                 ot, false, 1.f, beta, 0.f, 0.f), f);
+                 ot, false, 1.f, beta, 0.f, 0.f), f, true);
   }
 }
 

@@ -16,6 +16,18 @@ constexpr int PAD = 256;
 // Output element types (match ns_dtype values of the public header).
 enum OutType : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 
+// Row-pair layout of the internal fp16 matrices (rows even, leading
+// dimension ld a multiple of 32): element (i, j) sits at
+//   (i / 2) * 2 ld + (j / 32) * 64 + (i % 2) * 32 + j % 32,
+// i.e. every 128-byte line holds 32 consecutive columns of two neighbouring
+// rows. A GEMM K slice of 32 columns over 16 rows is then 8 whole lines
+// rather than 16 half lines of a row-major matrix, which lifts the
+// global -> LDS copy rate of gfx950 by about 1.5x. User buffers stay
+// row-major; the layout of every GEMM operand and output is a flag.
+__host__ __device__ inline int64_t pair_index(int64_t i, int64_t j, int64_t ld) {
+  return (i >> 1) * 2 * ld + (j >> 5) * 64 + (i & 1) * 32 + (j & 31);
+}
+
 // GEMM problem "NT": acc = A * B^T with A (M x K) and B (N x K) row-major
 // fp16, leading dimension K for both. Epilogue, evaluated in fp32:
 //   v = alpha * acc + beta * C[i][j] + (i == j && i < diag_n ? gamma : 0)
@@ -23,6 +35,9 @@ enum OutType : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 //   D2[i][j] = v + (i == j && i < diag_n ? delta : 0)      (fp16, ld N)
 //   DT[j][i] = v                       (fp16, transposed, leading dim M)
 // Stores to D are clipped to i < valid_m, j < valid_n.
+// Layouts: a_pairs / b_pairs / c_pairs select the row-pair layout (leading
+// dimension K for A and B, N for C) instead of row-major; d_pairs does the
+// same for D (ld ldd), D2 (ld N) and DT (ld M).
 // If c_is_bt: the caller guarantees C[i][j] == B[j][i] (C is B^T, which
 // needs M <= K), alpha != 0, and the kernel takes beta * C from the B
 // slices already in LDS during the K loop instead of reading C again.
@@ -43,6 +58,7 @@ struct GemmDesc {
   int out_type;
   int symmetric;
   int c_is_bt;
+  int a_pairs, b_pairs, c_pairs, d_pairs;
   int tile_begin;      // first logical tile of this problem in the launch
   int tiles;           // number of tiles of this problem
   int tiles_n;         // full: N / BN ; symmetric: M / BM
@@ -52,7 +68,8 @@ struct GemmDesc {
 // Normalisation of one matrix G (m x n, leading dim ldg, dtype g_type):
 // x = fp16(g / (||G||_F + eps)). The padded region [0, pm) x [0, pn) in G's
 // orientation is written: P[i][j] (ld ldp) and/or PT[j][i] (ld ldpt), zero
-// outside the real m x n block.
+// outside the real m x n block. If pairs, P and PT use the row-pair layout
+// (with ld ldp / ldpt), else row-major.
 struct NormDesc {
   const void* G;
   int64_t ldg;
@@ -63,6 +80,7 @@ struct NormDesc {
   int64_t ldp;
   _Float16* PT;
   int64_t ldpt;
+  int pairs;
   float eps;
   float* norm_out;     // optional copy of the norm (device)
   float* norm_slot;    // where the finalize kernel stores the norm
