@@ -351,6 +351,10 @@ __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Flo
             c[1][0] = lo_h(y0); c[1][1] = hi_h(y0); c[1][2] = lo_h(y1); c[1][3] = hi_h(y1);
           }
         }
+        // The diagonal term exists only in 32 x 32 blocks on the diagonal;
+        // the test is uniform, so other blocks skip the per-element compare.
+        const bool bdiag = MODE != EPI_SYM_OFFDIAG && e.gamma != 0.f &&
+                           rbase == col - (lane & 31) && rbase < e.diag_n;
         static_for<0, 2>([&](auto GG) {
           constexpr int g = g0 + GG;
           float v[4];
@@ -361,8 +365,14 @@ __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Flo
             if constexpr (SYM) x += e.beta * c[GG][q];
             if constexpr (MODE == EPI_FULL_C)
               x += e.beta * static_cast<float>(gmem(e.C)[lidx(e.c_pairs, row, col, e.N)]);
-            if (row == col && col < e.diag_n) x += e.gamma;
             v[q] = x;
+          }
+          if (bdiag) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int row = rbase + g * 8 + h * 4 + q;
+              if (row == col && col < e.diag_n) v[q] += e.gamma;
+            }
           }
           P[g][0] = pack_h2(v[0], v[1]);
           P[g][1] = pack_h2(v[2], v[3]);
