@@ -581,7 +581,8 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   const int nk = K / C::BK;
   auto kclamp = [&](int sl) { return min(sl, nk - 1) * C::BK; };
   static_for<0, STAGES>([&](auto s) { copy_my(s, kclamp(s)); });
-  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0) & ~0x0F00);
+  // only slice 0 is read before the next wait; slices 1-3 keep streaming
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * COPIES) & ~0x0F00);
   __builtin_amdgcn_s_barrier();
   if (grp == 0) {
     read_frags(stA(0), stB(0), fa0, fb0);
