@@ -147,6 +147,35 @@ ns_status ns_batched(const ns_matrix* mats, int count, ns_backend backend,
                      const ns_params* params, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* Column-sharded Gram NS on one matrix, the tensor-parallel route of the
+ * pages (Newton-Schulz reference page, section "Gram 空间 NS": R is a sum of
+ * local Gram matrices, so TP is exact through one all-reduce; article page,
+ * section "6. 与TP的结合", distributed mode: the norm from a scalar
+ * all-reduce of per-shard sums, and one Gram all-reduce per restart),
+ * emulated on one device with `shards` virtual shards:
+ *   * the working matrix X (s x l, short side first: columns of a wide G,
+ *     rows of a tall G) is split into `shards` column blocks, shard i
+ *     holding l / shards columns (one more for i < l % shards), each in its
+ *     own buffers;
+ *   * ||G||_F is formed over the whole matrix and shared by the shards;
+ *   * every shard forms its partial Gram matrix R_i = X_i X_i^T (fp16, all
+ *     shards in one launch); the all-reduce is a shard-order sum of the R_i
+ *     accumulated in fp32 and rounded once to fp16;
+ *   * the s x s Gram-space iteration runs once (every rank would hold an
+ *     identical copy); at a restart each shard applies Q to its own columns
+ *     and the partial Grams are reduced again; the output of shard i,
+ *     Q X_i, fills its own columns (wide) or rows (tall) of `out`.
+ * In exact arithmetic the result equals ns_gram's; with shards == 1 it is
+ * bitwise equal to ns_gram. 1 <= shards <= NS_MAX_SHARDS and
+ * shards <= max(m, n), else NS_ERR_INVALID_ARG; other arguments, the
+ * workspace and errors as for ns_gram (the size comes from
+ * ns_gram_sharded_workspace_size; `mat->g/out` are not read by it). */
+#define NS_MAX_SHARDS 64
+ns_status ns_gram_sharded_workspace_size(const ns_matrix* mat, int shards,
+                                         const ns_params* params, size_t* bytes);
+ns_status ns_gram_sharded(const ns_matrix* mat, int shards, const ns_params* params,
+                          void* ws, size_t ws_bytes, void* stream);
+
 /* Building blocks of the iteration, exposed for kernel-level testing.
  * All operands are fp16 row-major device matrices; products accumulate in
  * fp32 and the scaled sum is rounded once to fp16.
@@ -174,14 +203,17 @@ ns_status ns_gemm_nt(const void* a, const void* b, const void* c, void* d,
                      void* stream);
 
 /* Kernel timing (measurement aid). While enabled, every launch made by
- * ns_normalize / ns_gram / ns_direct / ns_batched is bracketed by two HIP
+ * ns_normalize / ns_gram / ns_gram_sharded / ns_direct / ns_batched is
+ * bracketed by two HIP
  * events on the caller's stream. ns_timing_read waits for the recorded
  * events, reports the totals since the last read, and clears them. The
  * algorithmic work counts exclude zero padding:
  *   gemm_flops   2 m n k per general product; s (s + 1) k per symmetric
  *                product (SYRK and the Gram-space products);
  *   norm_bytes   HBM bytes the normalisation must move: the input read
- *                twice (norm pass, scale pass) and two fp16 copies written.
+ *                twice (norm pass, scale pass) and two fp16 copies written;
+ *                the norm_* fields also count the shard reductions of
+ *                ns_gram_sharded (every part read once, the sum written).
  * Enabling or disabling is global to the process; disabled by default. */
 typedef struct {
   double gemm_ms;
@@ -202,6 +234,39 @@ const char* ns_status_string(ns_status s);
  * "查询当前后端"), e.g. "Gram NS / direct NS · kernel=hip-mfma-f16
  * (gfx950, 256 CUs)". Never NULL; valid until the next call. */
 const char* ns_backend_info(void);
+
+/* Structured diagnostics (the counterpart of the page's
+ * get_backend_status(), section "查询当前后端"): which device the calls
+ * would run on and which kernel set, so that "auto" is never ambiguous.
+ * Caller-owned struct, filled on the host; never launches work.
+ *   device_found     1 if the current HIP device is a gfx950, else 0
+ *                    (then every compute call returns NS_ERR_UNSUPPORTED);
+ *   device_index     current HIP device, -1 if none;
+ *   arch             gcnArchName of the current device ("" if none);
+ *   compute_units    CU count of the current device (0 if none);
+ *   clock_mhz        maximum engine clock reported by HIP (0 if none);
+ *   deterministic    always 1: fixed tile order, fixed reduction order and
+ *                    no floating-point atomics, so reruns on the same device
+ *                    and build are bitwise identical (the page's bit-exact
+ *                    option is therefore always on);
+ *   gemm_tile        edge of the GEMM workgroup tile;
+ *   version          NS_VERSION of the library;
+ *   kernel           static name of the kernel set (never NULL).
+ * Returns NS_ERR_INVALID_ARG for a NULL pointer, else NS_OK (also when no
+ * device is present: the struct then says so). */
+#define NS_VERSION 1
+typedef struct {
+  int device_found;
+  int device_index;
+  char arch[64];
+  int compute_units;
+  int clock_mhz;
+  int deterministic;
+  int gemm_tile;
+  int version;
+  const char* kernel;
+} ns_backend_status_t;
+ns_status ns_backend_status(ns_backend_status_t* out);
 
 #ifdef __cplusplus
 }

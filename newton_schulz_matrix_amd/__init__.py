@@ -74,6 +74,14 @@ class TimingReport(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class _BackendStatus(ctypes.Structure):
+    _fields_ = [("device_found", ctypes.c_int), ("device_index", ctypes.c_int),
+                ("arch", ctypes.c_char * 64), ("compute_units", ctypes.c_int),
+                ("clock_mhz", ctypes.c_int), ("deterministic", ctypes.c_int),
+                ("gemm_tile", ctypes.c_int), ("version", ctypes.c_int),
+                ("kernel", ctypes.c_char_p)]
+
+
 class _Matrix(ctypes.Structure):
     _fields_ = [("g", ctypes.c_void_p),
                 ("g_dtype", ctypes.c_int),
@@ -105,6 +113,8 @@ def library() -> ctypes.CDLL:
             "ns_direct": [M, P, vp, sz, vp],
             "ns_gram": [M, P, vp, sz, vp],
             "ns_batched": [M, ctypes.c_int, ctypes.c_int, P, vp, sz, vp],
+            "ns_gram_sharded_workspace_size": [M, ctypes.c_int, P, ctypes.POINTER(sz)],
+            "ns_gram_sharded": [M, ctypes.c_int, P, vp, sz, vp],
             "ns_syrk": [vp, i64, i64, vp, vp, sz, vp],
             "ns_gemm_nt": [vp, vp, vp, vp, i64, i64, i64, ctypes.c_float, ctypes.c_float,
                            ctypes.c_float, ctypes.c_int, vp, sz, vp],
@@ -121,6 +131,8 @@ def library() -> ctypes.CDLL:
         lib.ns_status_string.restype = ctypes.c_char_p
         lib.ns_backend_info.argtypes = []
         lib.ns_backend_info.restype = ctypes.c_char_p
+        lib.ns_backend_status.argtypes = [ctypes.POINTER(_BackendStatus)]
+        lib.ns_backend_status.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -131,6 +143,34 @@ def status_string(status: int) -> str:
 
 def ns_backend_info() -> str:
     return library().ns_backend_info().decode()
+
+
+def get_ns_backend() -> str:
+    """One-line summary for start-up logs (the page's get_ns_backend())."""
+    return ns_backend_info()
+
+
+def get_backend_status() -> dict:
+    """Diagnostics dictionary (the page's get_backend_status()).
+
+    ``auto_choice`` is the kernel set every call runs ("hip-mfma-f16") or
+    None when no gfx950 device is visible; ``deterministic`` is always True.
+    """
+    st = _BackendStatus()
+    _check(library().ns_backend_status(ctypes.byref(st)), "ns_backend_status")
+    found = bool(st.device_found)
+    return {
+        "arch": st.arch.decode(),
+        "device_index": st.device_index,
+        "compute_units": st.compute_units,
+        "clock_mhz": st.clock_mhz,
+        "gfx950_available": found,
+        "auto_choice": "hip-mfma-f16" if found else None,
+        "kernel": st.kernel.decode(),
+        "deterministic": bool(st.deterministic),
+        "gemm_tile": st.gemm_tile,
+        "version": st.version,
+    }
 
 
 def ns_timing_enable(enable: bool = True) -> None:
@@ -275,6 +315,27 @@ def ns_gram(G, coefficients=POLAR_EXPRESS_COEFFICIENTS,
     return out
 
 
+def ns_gram_sharded(G, shards: int, coefficients=POLAR_EXPRESS_COEFFICIENTS,
+                    restart_iterations: Iterable[int] = DEFAULT_RESTARTS,
+                    eps: float = DEFAULT_EPS, out_dtype=None):
+    """Gram NS of one matrix along the column-sharded (tensor-parallel) route,
+    with `shards` virtual shards on this device (see ns_gram_sharded in ns.h)."""
+    torch = _torch()
+    _device_tensor(G, "G")
+    out = torch.empty(G.shape, dtype=out_dtype or torch.float16, device=G.device)
+    mat = _matrix(G, out)
+    p, keep = _params(coefficients, restart_iterations, eps)
+    lib = library()
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.ns_gram_sharded_workspace_size(ctypes.byref(mat), int(shards), ctypes.byref(p),
+                                              ctypes.byref(nbytes)),
+           "ns_gram_sharded_workspace_size")
+    ws = _workspace(nbytes.value, G.device)
+    _check(lib.ns_gram_sharded(ctypes.byref(mat), int(shards), ctypes.byref(p), ws.data_ptr(),
+                               ws.numel(), _stream_ptr(G)), "ns_gram_sharded")
+    return out
+
+
 def ns_direct(G, coefficients=POLAR_EXPRESS_COEFFICIENTS, eps: float = DEFAULT_EPS,
               out_dtype=None, out=None, workspace=None):
     """Direct-space NS of one GPU matrix (the page's direct_newton_schulz)."""
@@ -354,3 +415,52 @@ def newton_schulz(G, backend: str = "gram", coefficients=POLAR_EXPRESS_COEFFICIE
     if backend == "direct":
         return ns_direct(G, coefficients, eps, out_dtype)
     raise ValueError(f"unknown backend {backend!r}")
+
+
+KERNELS = ("auto", "hip-mfma-f16")
+
+
+class NewtonSchulz:
+    """Configured NS operator (the page's NewtonSchulz(...) object).
+
+    backend: "gram" or "direct" (the algorithm axis). kernel: "auto" or
+    "hip-mfma-f16"; this build has one kernel set, so any other explicit
+    kernel name (the page's CUDA kernels among them) raises at construction,
+    as the page specifies for an unavailable explicit kernel, and so does an
+    explicit "hip-mfma-f16" when no gfx950 device is visible. deterministic:
+    accepted for interface parity; every call is bitwise reproducible anyway.
+    """
+
+    def __init__(self, backend: str = "gram", kernel: str = "auto",
+                 coefficients=POLAR_EXPRESS_COEFFICIENTS,
+                 restart_iterations: Iterable[int] = DEFAULT_RESTARTS,
+                 eps: float = DEFAULT_EPS, deterministic: bool = True):
+        if backend not in ("gram", "direct"):
+            raise ValueError(f"unknown backend {backend!r} (expected 'gram' or 'direct')")
+        if kernel not in KERNELS:
+            raise ValueError(f"kernel {kernel!r} is not available in this build "
+                             f"(available: {', '.join(KERNELS)})")
+        library()   # fails loudly when the library has not been built
+        if kernel != "auto" and not get_backend_status()["gfx950_available"]:
+            raise RuntimeError(f"kernel {kernel!r} needs a gfx950 device")
+        self.backend = backend
+        self.kernel = "hip-mfma-f16"
+        self.coefficients = tuple(tuple(float(x) for x in row) for row in coefficients)
+        self.restart_iterations = tuple(int(i) for i in restart_iterations)
+        self.eps = float(eps)
+        self.deterministic = True
+        # validate the table and restart indices once, on the host
+        ns_workspace_size([(1, 1)], backend, self.coefficients, self.restart_iterations,
+                          self.eps)
+
+    def __call__(self, G, out_dtype=None):
+        return newton_schulz(G, self.backend, self.coefficients, self.restart_iterations,
+                             self.eps, out_dtype)
+
+    def batched(self, Gs, outs=None, workspace=None, out_dtype=None):
+        return ns_batched(Gs, self.backend, self.coefficients, self.restart_iterations,
+                          self.eps, outs=outs, workspace=workspace, out_dtype=out_dtype)
+
+    def __repr__(self):
+        return (f"NewtonSchulz(backend={self.backend!r}, kernel={self.kernel!r}, "
+                f"steps={len(self.coefficients)}, restarts={self.restart_iterations})")

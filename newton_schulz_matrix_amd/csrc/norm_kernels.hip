@@ -200,7 +200,39 @@ __global__ __launch_bounds__(256) void cast_kernel(const NormDesc* __restrict__ 
   }
 }
 
+// Shard reduction: each thread sums 8 consecutive elements of every part
+// in index order (fp32), rounds once and stores 16 bytes.
+__global__ __launch_bounds__(256) void reduce_kernel(const ReduceDesc* __restrict__ descs,
+                                                     int count) {
+  const int b = blockIdx.x;
+  const int p = find_desc(count, b, [&](int i) { return descs[i].block_begin; });
+  const ReduceDesc& d = descs[p];
+  const int64_t i0 = static_cast<int64_t>(b - d.block_begin) * REDUCE_ELEMS + threadIdx.x * 8;
+  if (i0 >= d.elems) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < d.count; ++k) {
+    uint4 w = *reinterpret_cast<const uint4*>(d.parts[k] + i0);
+    _Float16 h[8];
+    __builtin_memcpy(h, &w, 16);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += static_cast<float>(h[e]);
+  }
+  _Float16 o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = static_cast<_Float16>(acc[e]);
+  uint4 w;
+  __builtin_memcpy(&w, o, 16);
+  *reinterpret_cast<uint4*>(d.out + i0) = w;
+}
+
 }  // namespace
+
+hipError_t launch_reduce(const ReduceDesc* descs, int count, int total_blocks,
+                         hipStream_t stream) {
+  if (total_blocks <= 0 || count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(reduce_kernel, dim3(total_blocks), dim3(256), 0, stream, descs, count);
+  return hipGetLastError();
+}
 
 hipError_t launch_sumsq(const NormDesc* descs, int count, int total_chunks,
                         hipStream_t stream) {

@@ -148,7 +148,7 @@ ns_status check_matrix(const ns_matrix& a) {
 // ----------------------------------------------------------------- planning
 
 struct Stage {
-  enum Kind { SUMSQ, FINALIZE, CAST, GEMM } kind;
+  enum Kind { SUMSQ, FINALIZE, CAST, GEMM, REDUCE } kind;
   size_t off;   // byte offset of its descriptors inside the table
   int count;    // descriptors
   int total;    // workgroups (chunks / tiles)
@@ -173,10 +173,19 @@ struct Probs {
 inline double sym_flops(int64_t s, int64_t k) { return double(s) * double(s + 1) * double(k); }
 inline double gen_flops(int64_t m, int64_t n, int64_t k) { return 2.0 * m * n * k; }
 
+// A column shard of the working matrix X (s x l, short side first): columns
+// [c0, c0 + lc) of X, i.e. columns of G when G is wide and rows of G when it
+// is tall. Every entry point but the sharded one uses a single shard.
+struct Shard {
+  int64_t c0, lc, Lp;      // first column, columns, padded columns
+  size_t X, XT[2], Rp;     // X_i (Sp x Lp), X_i^T (Lp x Sp) x2, partial Gram (Sp x Sp)
+};
+
 struct MatBuf {   // per-matrix workspace offsets (bytes from ws base)
   int64_t m, n, s, l, Sp, Lp;
   bool tall;
   size_t X, XT[2], R, Z, T, Q[2], A, B;
+  std::vector<Shard> sh;
   int chunks, chunks_n, chunk_begin;
 };
 
@@ -192,8 +201,10 @@ struct Plan {
 size_t sq_bytes(int64_t r, int64_t c) { return static_cast<size_t>(r) * c * 2; }
 
 // Workspace layout: per-matrix fp16 buffers, chunk partials, norms, then
-// the descriptor table (its size depends only on count and params).
-void layout(Plan& pl, const ns_matrix* mats, int count, ns_backend be) {
+// the descriptor table (its size depends only on count and params). With
+// shards > 1 (one matrix only) X, X^T and a partial Gram matrix exist per
+// shard; shard i has l / shards columns, one more for i < l % shards.
+void layout(Plan& pl, const ns_matrix* mats, int count, ns_backend be, int shards = 1) {
   size_t off = 0;
   pl.mats.resize(count);
   int chunk_begin = 0;
@@ -206,10 +217,25 @@ void layout(Plan& pl, const ns_matrix* mats, int count, ns_backend be) {
     b.l = std::max(b.m, b.n);
     b.Sp = pad_dim(b.s);
     b.Lp = pad_dim(b.l);
-    const size_t xl = sq_bytes(b.Sp, b.Lp), ss = sq_bytes(b.Sp, b.Sp);
-    b.X = off; off += xl;
-    b.XT[0] = off; off += xl;
-    b.XT[1] = off; off += xl;
+    const size_t ss = sq_bytes(b.Sp, b.Sp);
+    b.sh.resize(shards);
+    int64_t c0 = 0;
+    for (int k = 0; k < shards; ++k) {
+      Shard& h = b.sh[k];
+      h.c0 = c0;
+      h.lc = b.l / shards + (k < b.l % shards ? 1 : 0);
+      c0 += h.lc;
+      h.Lp = pad_dim(h.lc);
+      const size_t xl = sq_bytes(b.Sp, h.Lp);
+      h.X = off; off += xl;
+      h.XT[0] = off; off += xl;
+      h.XT[1] = off; off += xl;
+      h.Rp = 0;
+      if (shards > 1) { h.Rp = off; off += ss; }
+    }
+    b.X = b.sh[0].X;
+    b.XT[0] = b.sh[0].XT[0];
+    b.XT[1] = b.sh[0].XT[1];
     if (be == NS_GRAM) {
       b.R = off; off += ss;
       b.Z = off; off += ss;
@@ -276,6 +302,20 @@ struct Builder {
     }
     push(Stage::GEMM, v, begin, pr.flops);
   }
+
+  // One launch of shard reductions (HBM-bound: every part read once, the
+  // sum written once).
+  void reduce_stage(std::vector<ReduceDesc>& v) {
+    int begin = 0;
+    double bytes = 0.0;
+    for (auto& d : v) {
+      d.block_begin = begin;
+      d.blocks = ceil_div(d.elems, REDUCE_ELEMS);
+      begin += d.blocks;
+      bytes += double(d.elems) * 2.0 * (d.count + 1);
+    }
+    push(Stage::REDUCE, v, begin, bytes);
+  }
 };
 
 GemmDesc gemm(const _Float16* A, const _Float16* B, const _Float16* C, void* D,
@@ -312,17 +352,21 @@ GemmDesc c_from_b(GemmDesc d) {
   return d;
 }
 
-// Precision pipeline for every matrix: sum of squares, norm, scaled cast
-// into X (short side first) and X^T, zero-padded.
+inline size_t elem_bytes(ns_dtype t) { return t == NS_DT_F32 ? 4 : 2; }
+
+// Precision pipeline for every matrix: sum of squares and norm over the
+// whole matrix, then the scaled cast into X (short side first) and X^T,
+// zero-padded, per shard (a shard reads its own block of G and the whole
+// matrix's norm: the scalar all-reduce of a sharded run).
 void norm_stages(Builder& B, const ns_matrix* mats, float eps) {
   Plan& pl = B.pl;
-  std::vector<NormDesc> v;
+  std::vector<NormDesc> v, cast;
   int tile_begin = 0;
   double read_bytes = 0.0, write_bytes = 0.0;
   for (int i : pl.order) {
     const MatBuf& b = pl.mats[i];
     const double elems = double(b.m) * double(b.n);
-    read_bytes += elems * (mats[i].g_dtype == NS_DT_F32 ? 4.0 : 2.0);
+    read_bytes += elems * elem_bytes(mats[i].g_dtype);
     write_bytes += elems * 2.0 * 2.0;
     NormDesc d{};
     d.G = mats[i].g;
@@ -330,15 +374,6 @@ void norm_stages(Builder& B, const ns_matrix* mats, float eps) {
     d.g_type = out_code(mats[i].g_dtype);
     d.m = static_cast<int>(b.m);
     d.n = static_cast<int>(b.n);
-    if (!b.tall) {   // G is already short side first: G -> X, G^T -> X^T
-      d.pm = static_cast<int>(b.Sp); d.pn = static_cast<int>(b.Lp);
-      d.P = B.h(b.X); d.ldp = b.Lp;
-      d.PT = B.h(b.XT[0]); d.ldpt = b.Sp;
-    } else {         // tall: G -> X^T, G^T -> X
-      d.pm = static_cast<int>(b.Lp); d.pn = static_cast<int>(b.Sp);
-      d.P = B.h(b.XT[0]); d.ldp = b.Sp;
-      d.PT = B.h(b.X); d.ldpt = b.Lp;
-    }
     d.eps = eps;
     d.pairs = 1;
     d.norm_out = nullptr;
@@ -347,11 +382,29 @@ void norm_stages(Builder& B, const ns_matrix* mats, float eps) {
     d.chunk_begin = b.chunk_begin;
     d.chunks = b.chunks;
     d.chunks_n = b.chunks_n;
-    d.tiles_n = ceil_div(d.pn, CAST_TILE);
-    d.tiles = ceil_div(d.pm, CAST_TILE) * d.tiles_n;
-    d.tile_begin = tile_begin;
-    tile_begin += d.tiles;
     v.push_back(d);
+    for (const Shard& h : b.sh) {
+      NormDesc c = d;
+      const size_t off = static_cast<size_t>(h.c0) * elem_bytes(mats[i].g_dtype) *
+                         (b.tall ? static_cast<size_t>(mats[i].ldg) : 1);
+      c.G = mats[i].g ? static_cast<const unsigned char*>(mats[i].g) + off : nullptr;
+      if (!b.tall) {   // G is already short side first: G -> X, G^T -> X^T
+        c.n = static_cast<int>(h.lc);
+        c.pm = static_cast<int>(b.Sp); c.pn = static_cast<int>(h.Lp);
+        c.P = B.h(h.X); c.ldp = h.Lp;
+        c.PT = B.h(h.XT[0]); c.ldpt = b.Sp;
+      } else {         // tall: G -> X^T, G^T -> X
+        c.m = static_cast<int>(h.lc);
+        c.pm = static_cast<int>(h.Lp); c.pn = static_cast<int>(b.Sp);
+        c.P = B.h(h.XT[0]); c.ldp = b.Sp;
+        c.PT = B.h(h.X); c.ldpt = h.Lp;
+      }
+      c.tiles_n = ceil_div(c.pn, CAST_TILE);
+      c.tiles = ceil_div(c.pm, CAST_TILE) * c.tiles_n;
+      c.tile_begin = tile_begin;
+      tile_begin += c.tiles;
+      cast.push_back(c);
+    }
   }
   // sumsq chunks are indexed by the chunk_begin of the matrix order in the
   // layout; re-sort the descriptor copy for the chunk search.
@@ -360,23 +413,27 @@ void norm_stages(Builder& B, const ns_matrix* mats, float eps) {
             [](const NormDesc& a, const NormDesc& b) { return a.chunk_begin < b.chunk_begin; });
   B.push(Stage::SUMSQ, by_chunk, pl.total_chunks, read_bytes);
   B.push(Stage::FINALIZE, v, static_cast<int>(v.size()), 0.0);
-  B.push(Stage::CAST, v, tile_begin, read_bytes + write_bytes);
+  B.push(Stage::CAST, cast, tile_begin, read_bytes + write_bytes);
 }
 
-void final_output(Builder& B, const ns_matrix& mt, const MatBuf& b, const _Float16* Qm,
-                  const _Float16* XT, const _Float16* Xc, const _Float16* XTc, float beta,
-                  Probs& out) {
+void final_output(Builder& B, const ns_matrix& mt, const MatBuf& b, const Shard& h,
+                  const _Float16* Qm, const _Float16* XT, const _Float16* Xc,
+                  const _Float16* XTc, float beta, Probs& out) {
   // wide: out = Q X = Q (X^T)^T                    (M = Sp, N = Lp)
   // tall: out = (Q X)^T = X^T Q^T = X^T Q (Q sym.)  (M = Lp, N = Sp)
   // (direct backend: Q is the step matrix b A + c A^2 and the epilogue adds
-  //  beta times X or X^T)
+  //  beta times X or X^T). A shard writes its own columns (wide) or rows
+  // (tall) of the caller's output.
   const int ot = out_code(mt.out_dtype);
-  const double f = gen_flops(b.s, b.l, b.s);
+  const double f = gen_flops(b.s, h.lc, b.s);
+  const size_t step = elem_bytes(mt.out_dtype) * (b.tall ? static_cast<size_t>(mt.ldo) : 1);
+  void* o = mt.out ? static_cast<unsigned char*>(mt.out) + static_cast<size_t>(h.c0) * step
+                   : nullptr;
   if (!b.tall) {
-    out.add(c_from_b(gemm(Qm, XT, Xc, mt.out, nullptr, nullptr, b.Sp, b.Lp, b.Sp, mt.ldo, b.m,
-                          b.n, 0, ot, false, 1.f, beta, 0.f, 0.f)), f, true);
+    out.add(c_from_b(gemm(Qm, XT, Xc, o, nullptr, nullptr, b.Sp, h.Lp, b.Sp, mt.ldo, b.m,
+                          h.lc, 0, ot, false, 1.f, beta, 0.f, 0.f)), f, true);
   } else {
-    out.add(gemm(XT, Qm, XTc, mt.out, nullptr, nullptr, b.Lp, b.Sp, b.Sp, mt.ldo, b.m, b.n, 0,
+    out.add(gemm(XT, Qm, XTc, o, nullptr, nullptr, h.Lp, b.Sp, b.Sp, mt.ldo, h.lc, b.n, 0,
                  ot, false, 1.f, beta, 0.f, 0.f), f, true);
   }
 }
@@ -387,15 +444,33 @@ void gram_stages(Builder& B, const ns_matrix* mats, const ns_params& p) {
   std::vector<bool> restart(K, false);
   for (int i = 0; i < p.num_restarts; ++i) restart[p.restarts[i]] = true;
 
+  // R = X X^T. A sharded matrix forms one partial Gram matrix per shard
+  // (all shards in the same launch, as on separate devices), then their
+  // shard-order sum: R = sum_i X_i X_i^T, the exact TP decomposition.
   auto syrk_all = [&](int /*unused*/) {
     Probs v;
+    std::vector<ReduceDesc> red;
     for (int i : pl.order) {
       const MatBuf& b = pl.mats[i];
-      v.add(gemm(B.h(b.X), B.h(b.X), nullptr, B.h(b.R), nullptr, nullptr, b.Sp, b.Sp, b.Lp,
-                 b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, 0.f, 0.f, 0.f),
-            sym_flops(b.s, b.l));
+      if (b.sh.size() == 1) {
+        v.add(gemm(B.h(b.X), B.h(b.X), nullptr, B.h(b.R), nullptr, nullptr, b.Sp, b.Sp, b.Lp,
+                   b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, 0.f, 0.f, 0.f),
+              sym_flops(b.s, b.l));
+        continue;
+      }
+      ReduceDesc r{};
+      for (const Shard& h : b.sh) {
+        v.add(gemm(B.h(h.X), B.h(h.X), nullptr, B.h(h.Rp), nullptr, nullptr, b.Sp, b.Sp, h.Lp,
+                   b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, 0.f, 0.f, 0.f),
+              sym_flops(b.s, h.lc));
+        r.parts[r.count++] = B.h(h.Rp);
+      }
+      r.out = B.h(b.R);
+      r.elems = b.Sp * b.Sp;
+      red.push_back(r);
     }
     B.gemm_stage(v);
+    B.reduce_stage(red);
   };
 
   norm_stages(B, mats, p.eps);
@@ -409,9 +484,11 @@ void gram_stages(Builder& B, const ns_matrix* mats, const ns_params& p) {
       Probs v;
       for (int i : pl.order) {
         const MatBuf& b = pl.mats[i];
-        v.add(gemm(B.h(b.Q[qc]), B.h(b.XT[xt]), nullptr, B.h(b.X), nullptr, B.h(b.XT[xt ^ 1]),
-                   b.Sp, b.Lp, b.Sp, b.Lp, b.Sp, b.Lp, 0, OUT_F16, false, 1.f, 0.f, 0.f, 0.f),
-              gen_flops(b.s, b.l, b.s));
+        for (const Shard& h : b.sh)   // each shard applies Q to its own columns
+          v.add(gemm(B.h(b.Q[qc]), B.h(h.XT[xt]), nullptr, B.h(h.X), nullptr,
+                     B.h(h.XT[xt ^ 1]), b.Sp, h.Lp, b.Sp, h.Lp, b.Sp, h.Lp, 0, OUT_F16, false,
+                     1.f, 0.f, 0.f, 0.f),
+                gen_flops(b.s, h.lc, b.s));
       }
       B.gemm_stage(v);
       xt ^= 1;
@@ -470,7 +547,8 @@ void gram_stages(Builder& B, const ns_matrix* mats, const ns_params& p) {
   Probs v;
   for (int i : pl.order) {
     const MatBuf& b = pl.mats[i];
-    final_output(B, mats[i], b, B.h(b.Q[qc]), B.h(b.XT[xt]), nullptr, nullptr, 0.f, v);
+    for (const Shard& h : b.sh)
+      final_output(B, mats[i], b, h, B.h(b.Q[qc]), B.h(h.XT[xt]), nullptr, nullptr, 0.f, v);
   }
   B.gemm_stage(v);
 }
@@ -500,7 +578,8 @@ void direct_stages(Builder& B, const ns_matrix* mats, const ns_params& p) {
                              false, 1.f, a, 0.f, 0.f)),
                gen_flops(b.s, b.l, b.s));
       } else {
-        final_output(B, mats[i], b, B.h(b.B), B.h(b.XT[xt]), B.h(b.X), B.h(b.XT[xt]), a, v3);
+        final_output(B, mats[i], b, b.sh[0], B.h(b.B), B.h(b.XT[xt]), B.h(b.X), B.h(b.XT[xt]),
+                     a, v3);
       }
     }
     B.gemm_stage(v1);
@@ -511,8 +590,8 @@ void direct_stages(Builder& B, const ns_matrix* mats, const ns_params& p) {
 }
 
 ns_status build_plan(Plan& pl, const ns_matrix* mats, int count, ns_backend be,
-                     const ns_params& p, unsigned char* ws) {
-  layout(pl, mats, count, be);
+                     const ns_params& p, unsigned char* ws, int shards = 1) {
+  layout(pl, mats, count, be, shards);
   Builder B(pl, ws);
   if (be == NS_GRAM) gram_stages(B, mats, p);
   else direct_stages(B, mats, p);
@@ -595,6 +674,12 @@ ns_status run_plan(const Plan& pl, unsigned char* ws, hipStream_t stream) {
                              st.total, stream);
         });
         break;
+      case Stage::REDUCE:
+        e = timed(on, false, st.work, stream, [&] {
+          return launch_reduce(reinterpret_cast<const ReduceDesc*>(table + st.off), st.count,
+                               st.total, stream);
+        });
+        break;
     }
     if (e != hipSuccess) return NS_ERR_HIP;
   }
@@ -614,18 +699,24 @@ ns_status check_call(const ns_matrix* mats, int count, ns_backend be, const ns_p
   return NS_OK;
 }
 
+ns_status check_shards(const ns_matrix& a, int shards) {
+  if (shards < 1 || shards > MAX_SHARDS) return NS_ERR_INVALID_ARG;
+  if (shards > std::max(a.m, a.n)) return NS_ERR_INVALID_ARG;
+  return NS_OK;
+}
+
 ns_status run_batched(const ns_matrix* mats, int count, ns_backend be, const ns_params* p,
-                      void* ws, size_t ws_bytes, void* stream) {
+                      void* ws, size_t ws_bytes, void* stream, int shards = 1) {
   ns_status s = check_call(mats, count, be, p);
   if (s != NS_OK) return s;
   if (count == 0) return NS_OK;
   Plan sizing;
-  build_plan(sizing, mats, count, be, *p, nullptr);
+  build_plan(sizing, mats, count, be, *p, nullptr, shards);
   if (!ws || ws_bytes < sizing.total) return NS_ERR_WORKSPACE;
   s = check_device();
   if (s != NS_OK) return s;
   Plan pl;
-  build_plan(pl, mats, count, be, *p, static_cast<unsigned char*>(ws));
+  build_plan(pl, mats, count, be, *p, static_cast<unsigned char*>(ws), shards);
   return run_plan(pl, static_cast<unsigned char*>(ws), static_cast<hipStream_t>(stream));
 }
 
@@ -668,6 +759,33 @@ NS_API const char* ns_backend_info(void) {
   std::lock_guard<std::mutex> lock(g_dev_mu);
   g_info = buf;
   return g_info.c_str();
+}
+
+NS_API ns_status ns_backend_status(ns_backend_status_t* out) {
+  if (!out) return NS_ERR_INVALID_ARG;
+  std::memset(out, 0, sizeof(*out));
+  out->device_index = -1;
+  out->deterministic = 1;
+  out->gemm_tile = gemm_tile();
+  out->version = NS_VERSION;
+  out->kernel = "hip-mfma-f16 grouped NT GEMM (256x256 tiles, ping-pong waves, row-pair layout)";
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return NS_OK;
+  }
+  int dev = -1;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return NS_OK;
+  }
+  out->device_index = dev;
+  std::snprintf(out->arch, sizeof(out->arch), "%s", prop.gcnArchName);
+  out->compute_units = prop.multiProcessorCount;
+  out->clock_mhz = prop.clockRate / 1000;
+  out->device_found = check_device() == NS_OK ? 1 : 0;
+  return NS_OK;
 }
 
 NS_API ns_status ns_timing_enable(int enable) {
@@ -733,6 +851,27 @@ NS_API ns_status ns_gram(const ns_matrix* mat, const ns_params* params, void* ws
                          size_t ws_bytes, void* stream) {
   if (!mat) return NS_ERR_INVALID_ARG;
   return run_batched(mat, 1, NS_GRAM, params, ws, ws_bytes, stream);
+}
+
+NS_API ns_status ns_gram_sharded_workspace_size(const ns_matrix* mat, int shards,
+                                                const ns_params* params, size_t* bytes) {
+  if (!bytes || !mat) return NS_ERR_INVALID_ARG;
+  ns_status s = check_params(params, NS_GRAM);
+  if (s == NS_OK) s = check_matrix_shape(*mat);
+  if (s == NS_OK) s = check_shards(*mat, shards);
+  if (s != NS_OK) return s;
+  Plan pl;
+  build_plan(pl, mat, 1, NS_GRAM, *params, nullptr, shards);
+  *bytes = pl.total;
+  return NS_OK;
+}
+
+NS_API ns_status ns_gram_sharded(const ns_matrix* mat, int shards, const ns_params* params,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  if (!mat) return NS_ERR_INVALID_ARG;
+  ns_status s = check_shards(*mat, shards);
+  if (s != NS_OK) return s;
+  return run_batched(mat, 1, NS_GRAM, params, ws, ws_bytes, stream, shards);
 }
 
 NS_API ns_status ns_direct(const ns_matrix* mat, const ns_params* params, void* ws,

@@ -99,6 +99,21 @@ constexpr int SQ_COLS = 256;
 // Cast tile.
 constexpr int CAST_TILE = 64;
 
+// Sum of `count` fp16 buffers of `elems` elements each (same layout),
+// accumulated in fp32 in index order and rounded once to fp16. It stands in
+// for the all-reduce of per-shard partial Gram matrices when one matrix is
+// processed as column shards.
+constexpr int MAX_SHARDS = 64;
+constexpr int REDUCE_ELEMS = 2048;   // elements per workgroup (256 threads x 8)
+struct ReduceDesc {
+  const _Float16* parts[MAX_SHARDS];
+  _Float16* out;
+  int64_t elems;       // multiple of 8
+  int count;
+  int block_begin;     // first workgroup of this reduction in the launch
+  int blocks;
+};
+
 // Launchers (all enqueue on `stream`; return hipSuccess or the launch error).
 hipError_t launch_sumsq(const NormDesc* descs, int count, int total_chunks,
                         hipStream_t stream);
@@ -108,6 +123,8 @@ hipError_t launch_cast(const NormDesc* descs, int count, int total_tiles,
                        hipStream_t stream);
 hipError_t launch_gemm(const GemmDesc* descs, int count, int total_tiles,
                        hipStream_t stream);
+hipError_t launch_reduce(const ReduceDesc* descs, int count, int total_blocks,
+                         hipStream_t stream);
 
 // Tile edge of the GEMM kernel (BM == BN), and the multiple that every K
 // must be (the kernel's LDS ring consumes K in STAGES slices of BK).

@@ -23,6 +23,8 @@ from .ns_oracle import (  # noqa: F401
     normalize,
     direct_newton_schulz,
     gram_newton_schulz,
+    gram_newton_schulz_sharded,
+    shard_bounds,
     closed_form,
     scalar_map,
     step_maps,

@@ -36,6 +36,11 @@ Readings taken where the page is silent (each is listed in the design notes):
   from X_{k+1} = (a_k I + Z_k) X_k; it is skipped when R_{k+1} is not used
   (after the last step, or when step k+1 restarts).
 
+``gram_newton_schulz_sharded`` takes the tensor-parallel route of the same
+iteration (X split by columns, R as the sum of per-shard Gram matrices,
+per-shard restarts and outputs): the pages' exact-TP statement in section
+"Gram 空间 NS", and section "6. 与TP的结合" of the distributed-Muon article.
+
 Parity pins (tests/test_oracle_pins.py): gram == direct in fp64, the SVD
 closed form ``closed_form`` (singular values mapped by the composed scalar
 polynomial, singular vectors kept), restart invariance, and special cases
@@ -138,6 +143,68 @@ def gram_newton_schulz(G, coefficients=POLAR_EXPRESS_COEFFICIENTS,
             M = a * eye + Z
             R = M @ R @ M
     out = Q @ X
+    return out.T.copy() if transposed else out
+
+
+def shard_bounds(l: int, shards: int):
+    """Column blocks of the short-side-first X for `shards` shards.
+
+    Shard i holds l // shards columns, one more for i < l % shards (the
+    plainest balanced split; the pages fix no split).
+    """
+    if shards < 1 or shards > l:
+        raise ValueError("need 1 <= shards <= l")
+    bounds, c0 = [], 0
+    for i in range(shards):
+        lc = l // shards + (1 if i < l % shards else 0)
+        bounds.append((c0, c0 + lc))
+        c0 += lc
+    return bounds
+
+
+def gram_newton_schulz_sharded(G, coefficients=POLAR_EXPRESS_COEFFICIENTS,
+                               restart_iterations=DEFAULT_RESTARTS, shards: int = 2,
+                               eps: float = DEFAULT_EPS) -> np.ndarray:
+    """Gram-space NS along the tensor-parallel route, shard by shard.
+
+    Follows the Newton-Schulz reference page, section "Gram 空间 NS" (R is a
+    sum of local Gram matrices, so TP is exact through one all-reduce), and
+    the article page, section "6. 与TP的结合" (distributed mode: the norm
+    from a scalar all-reduce of per-shard sums of squares; one Gram
+    all-reduce whenever X changes). X is split by columns into X_1..X_T;
+    every "all-reduce" is a plain sum over shards; the s x s iteration is
+    the unsharded one; each shard applies Q to its own columns.
+    """
+    G = _as_f64(G)
+    transposed = G.shape[0] > G.shape[1]
+    Xfull = G.T if transposed else G
+    blocks = shard_bounds(Xfull.shape[1], shards)
+    parts = [Xfull[:, a:b] for a, b in blocks]
+    # scalar all-reduce of the per-shard sums of squares
+    norm = float(np.sqrt(sum(float(np.sum(P * P)) for P in parts)))
+    Xs = [P / (norm + eps) for P in parts]
+    K = len(coefficients)
+    restarts = set(int(i) for i in restart_iterations)
+    if any(i < 0 or i >= K for i in restarts):
+        raise ValueError("restart index out of range")
+    eye = np.eye(Xfull.shape[0])
+
+    def gram(Xs):   # all-reduce of the local Gram matrices
+        return sum(Xi @ Xi.T for Xi in Xs)
+
+    R = gram(Xs)
+    Q = None
+    for k, (a, b, c) in enumerate(coefficients):
+        if k in restarts and Q is not None:
+            Xs = [Q @ Xi for Xi in Xs]
+            R = gram(Xs)
+            Q = None
+        Z = b * R + c * (R @ R)
+        Q = Z + a * eye if Q is None else Z @ Q + a * Q
+        if k + 1 < K and (k + 1) not in restarts:
+            M = a * eye + Z
+            R = M @ R @ M
+    out = np.concatenate([Q @ Xi for Xi in Xs], axis=1)
     return out.T.copy() if transposed else out
 
 

@@ -205,3 +205,44 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(nsmi, "LIB_PATH", "/nonexistent/libnsmi.so")
     with pytest.raises(RuntimeError, match="missing"):
         nsmi.library()
+
+
+def _sharded_size(m, n, shards, restarts=(2,)):
+    lib = nsmi.library()
+    p, keep = _params(restarts=restarts)
+    mat = nsmi._Matrix(None, nsmi.NS_DT_F32, m, n, n, None, nsmi.NS_DT_F16, n)
+    nb = ctypes.c_size_t(0)
+    st = lib.ns_gram_sharded_workspace_size(ctypes.byref(mat), shards, ctypes.byref(p),
+                                            ctypes.byref(nb))
+    return st, nb.value
+
+
+def test_sharded_workspace_rules():
+    st1, one = _sharded_size(256, 1024, 1)
+    assert st1 == nsmi.NS_OK
+    assert one == _size([(256, 1024)])             # one shard: the ns_gram layout
+    st4, four = _sharded_size(256, 1024, 4)
+    assert st4 == nsmi.NS_OK and four > one        # partial Grams and padded shards
+    assert _sharded_size(1024, 256, 4)[1] == four  # tall and wide alike
+    for bad in (0, -1, 65, 1025):                  # range and shards <= max(m, n)
+        assert _sharded_size(256, 1024, bad)[0] == nsmi.NS_ERR_INVALID_ARG
+    assert _sharded_size(3, 5, 5)[0] == nsmi.NS_OK
+    assert _sharded_size(3, 5, 6)[0] == nsmi.NS_ERR_INVALID_ARG
+    assert _sharded_size(16, 32, 2, restarts=(7,))[0] == nsmi.NS_ERR_INVALID_ARG
+
+
+def test_sharded_call_rejects_bad_arguments_before_any_device_work():
+    lib = nsmi.library()
+    p, keep = _params()
+    fake = 0x1000
+    good = _mats([(16, 32)], fake, fake)
+    assert lib.ns_gram_sharded(None, 2, ctypes.byref(p), fake, 1 << 30, None) \
+        == nsmi.NS_ERR_INVALID_ARG
+    assert lib.ns_gram_sharded(good, 0, ctypes.byref(p), fake, 1 << 30, None) \
+        == nsmi.NS_ERR_INVALID_ARG
+    assert lib.ns_gram_sharded(good, 33, ctypes.byref(p), fake, 1 << 30, None) \
+        == nsmi.NS_ERR_INVALID_ARG
+    assert lib.ns_gram_sharded(good, 2, ctypes.byref(p), fake, 16, None) \
+        == nsmi.NS_ERR_WORKSPACE
+    assert lib.ns_gram_sharded(_mats([(16, 32)], None, fake), 2, ctypes.byref(p), fake,
+                               1 << 30, None) == nsmi.NS_ERR_INVALID_ARG

@@ -1,0 +1,90 @@
+"""GPU parity of the column-sharded (tensor-parallel) Gram route,
+ns_gram_sharded, emulated with virtual shards on one device.
+
+* one shard is bitwise equal to ns_gram (same layout, same launches);
+* T shards against the fp64 oracle (gram_newton_schulz_sharded, pinned to
+  the closed form) at the 1e-2 bar, and within 1.5x (+1e-3) of the
+  unsharded GPU result's own error: the only arithmetic that differs is the
+  partial Gram products and their shard-order fp32 sum;
+* ragged splits, tall and wide, restart patterns, fp32 output, 64 shards;
+* a full-size Llama-3-8B gate projection (14336 x 4096) at TP = 4.
+"""
+
+import pytest
+import torch
+
+import newton_schulz_matrix_amd as nsmi
+import workloads as W
+from gpu_helpers import rel_fro, require_gpu, to64
+from oracle import YOU_COEFFICIENTS, POLAR_EXPRESS_COEFFICIENTS, gram_newton_schulz_sharded
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("shape", [(300, 1000), (1000, 300), (256, 256), (7, 13)])
+def test_one_shard_is_bitwise_ns_gram(shape):
+    require_gpu()
+    G = W.small_gaussian(31, *shape).cuda()
+    a = nsmi.ns_gram_sharded(G, 1, nsmi.YOU_COEFFICIENTS, (2,))
+    b = nsmi.ns_gram(G, nsmi.YOU_COEFFICIENTS, (2,))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("shape", [(300, 1000), (1000, 300), (257, 513), (640, 2000)])
+@pytest.mark.parametrize("shards", [2, 3, 4, 7])
+def test_sharded_against_oracle(shape, shards):
+    require_gpu()
+    print(f"sharded {shape} x{shards}", flush=True)
+    G = W.small_gaussian(shards, *shape)
+    got = nsmi.ns_gram_sharded(G.cuda(), shards, nsmi.YOU_COEFFICIENTS, (2,))
+    ref_gpu = nsmi.ns_gram(G.cuda(), nsmi.YOU_COEFFICIENTS, (2,))
+    torch.cuda.synchronize()
+    want = gram_newton_schulz_sharded(to64(G), YOU_COEFFICIENTS, (2,), shards)
+    err = rel_fro(to64(got), want)
+    base = rel_fro(to64(ref_gpu), want)
+    print(f"  err {err:.3e}, unsharded {base:.3e}", flush=True)
+    assert err <= 1e-2
+    assert err <= 1.5 * base + 1e-3
+
+
+@pytest.mark.parametrize("restarts", [(), (1, 3), (1, 2, 3, 4)])
+def test_sharded_restart_patterns(restarts):
+    require_gpu()
+    G = W.small_gaussian(3, 384, 1000)
+    got = nsmi.ns_gram_sharded(G.cuda(), 3, nsmi.YOU_COEFFICIENTS, restarts)
+    torch.cuda.synchronize()
+    want = gram_newton_schulz_sharded(to64(G), YOU_COEFFICIENTS, restarts, 3)
+    assert rel_fro(to64(got), want) <= 1e-2
+
+
+def test_sharded_fp32_output_and_many_shards():
+    require_gpu()
+    G = W.small_gaussian(8, 64, 300)
+    got = nsmi.ns_gram_sharded(G.cuda(), 64, nsmi.YOU_COEFFICIENTS, (2,),
+                               out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert got.dtype == torch.float32
+    want = gram_newton_schulz_sharded(to64(G), YOU_COEFFICIENTS, (2,), 64)
+    assert rel_fro(to64(got), want) <= 1e-2
+
+
+def test_sharded_is_deterministic():
+    require_gpu()
+    G = W.small_gaussian(9, 512, 1500).cuda()
+    a = nsmi.ns_gram_sharded(G, 5, nsmi.YOU_COEFFICIENTS, (2,))
+    b = nsmi.ns_gram_sharded(G, 5, nsmi.YOU_COEFFICIENTS, (2,))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_llama_gate_projection_tp4():
+    require_gpu()
+    j = W.WORKLOADS[3].labels.index("gate_proj")
+    G = W.matrix(3, j)
+    got = nsmi.ns_gram_sharded(G.cuda(), 4, nsmi.POLAR_EXPRESS_COEFFICIENTS, (2,))
+    torch.cuda.synchronize()
+    want = gram_newton_schulz_sharded(to64(G), POLAR_EXPRESS_COEFFICIENTS, (2,), 4)
+    err = rel_fro(to64(got), want)
+    print(f"gate {tuple(G.shape)} TP=4: rel err {err:.3e}", flush=True)
+    assert err <= 1e-2
