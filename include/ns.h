@@ -176,6 +176,50 @@ ns_status ns_gram_sharded_workspace_size(const ns_matrix* mat, int shards,
 ns_status ns_gram_sharded(const ns_matrix* mat, int shards, const ns_params* params,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* One Muon optimizer step around the NS call, Gram backend, for a batch of
+ * matrices (one launch per stage, like ns_batched). The article page
+ * (section "1. Introduction", "2. Muon执行过程") says a Muon step keeps a
+ * momentum M of the gradient, orthogonalises M approximately and uses the
+ * result as the update direction; its formula itself is missing from the
+ * extracted text, and the pages give only lr = 0.02 as an example. This
+ * entry takes the plainest reading of that description:
+ *   M <- beta * M + G                 (momentum, elementwise)
+ *   W <- W - lr * scale * NS(M)       (NS = the Gram iteration of ns_gram
+ *                                      on the updated M, same params)
+ * with beta, lr and a per-matrix scale chosen by the caller (no value of
+ * them is fixed by the pages; scale = 1 gives the plain update).
+ * Fusion: the momentum update runs inside the norm pass (M read, updated
+ * with one fp32 fma per element, rounded to M's type and written back, and
+ * the norm taken of the stored values); the parameter update runs in the
+ * epilogue of the final product (W read as C and written as D, the fp32
+ * product Q X scaled by -lr * scale and added before W's one rounding), so
+ * NS(M) is never stored.
+ *   grad      (m, n) row-major, fp32/bf16/fp16, leading dim ld_grad, read;
+ *   momentum  (m, n) row-major, any of the three types, ld_momentum, read
+ *             and written;
+ *   param     (m, n) row-major, any of the three types, ld_param, read and
+ *             written.
+ * The three buffers of a matrix must not overlap each other or another
+ * matrix's. Validation, workspace (ns_muon_workspace_size; pointers are not
+ * read by it), streams, errors and determinism as for ns_batched; beta,
+ * lr and every scale must be finite. */
+typedef struct {
+  const void* grad;
+  ns_dtype grad_dtype;
+  int64_t m, n, ld_grad;
+  void* momentum;
+  ns_dtype momentum_dtype;
+  int64_t ld_momentum;
+  void* param;
+  ns_dtype param_dtype;
+  int64_t ld_param;
+  float scale;
+} ns_muon_matrix;
+ns_status ns_muon_workspace_size(const ns_muon_matrix* mats, int count,
+                                 const ns_params* params, size_t* bytes);
+ns_status ns_muon_step(const ns_muon_matrix* mats, int count, const ns_params* params,
+                       float beta, float lr, void* ws, size_t ws_bytes, void* stream);
+
 /* Building blocks of the iteration, exposed for kernel-level testing.
  * All operands are fp16 row-major device matrices; products accumulate in
  * fp32 and the scaled sum is rounded once to fp16.

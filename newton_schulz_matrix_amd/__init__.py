@@ -82,6 +82,15 @@ class _BackendStatus(ctypes.Structure):
                 ("kernel", ctypes.c_char_p)]
 
 
+class _MuonMatrix(ctypes.Structure):
+    _fields_ = [("grad", ctypes.c_void_p), ("grad_dtype", ctypes.c_int),
+                ("m", ctypes.c_int64), ("n", ctypes.c_int64), ("ld_grad", ctypes.c_int64),
+                ("momentum", ctypes.c_void_p), ("momentum_dtype", ctypes.c_int),
+                ("ld_momentum", ctypes.c_int64),
+                ("param", ctypes.c_void_p), ("param_dtype", ctypes.c_int),
+                ("ld_param", ctypes.c_int64), ("scale", ctypes.c_float)]
+
+
 class _Matrix(ctypes.Structure):
     _fields_ = [("g", ctypes.c_void_p),
                 ("g_dtype", ctypes.c_int),
@@ -115,6 +124,10 @@ def library() -> ctypes.CDLL:
             "ns_batched": [M, ctypes.c_int, ctypes.c_int, P, vp, sz, vp],
             "ns_gram_sharded_workspace_size": [M, ctypes.c_int, P, ctypes.POINTER(sz)],
             "ns_gram_sharded": [M, ctypes.c_int, P, vp, sz, vp],
+            "ns_muon_workspace_size": [ctypes.POINTER(_MuonMatrix), ctypes.c_int, P,
+                                       ctypes.POINTER(sz)],
+            "ns_muon_step": [ctypes.POINTER(_MuonMatrix), ctypes.c_int, P, ctypes.c_float,
+                             ctypes.c_float, vp, sz, vp],
             "ns_syrk": [vp, i64, i64, vp, vp, sz, vp],
             "ns_gemm_nt": [vp, vp, vp, vp, i64, i64, i64, ctypes.c_float, ctypes.c_float,
                            ctypes.c_float, ctypes.c_int, vp, sz, vp],
@@ -334,6 +347,43 @@ def ns_gram_sharded(G, shards: int, coefficients=POLAR_EXPRESS_COEFFICIENTS,
     _check(lib.ns_gram_sharded(ctypes.byref(mat), int(shards), ctypes.byref(p), ws.data_ptr(),
                                ws.numel(), _stream_ptr(G)), "ns_gram_sharded")
     return out
+
+
+def ns_muon_step(grads: List, momenta: List, params: List, beta: float, lr: float,
+                 scales: Optional[List[float]] = None,
+                 coefficients=POLAR_EXPRESS_COEFFICIENTS,
+                 restart_iterations: Iterable[int] = DEFAULT_RESTARTS,
+                 eps: float = DEFAULT_EPS, workspace=None) -> None:
+    """One Muon step, in place: M <- beta M + G, W <- W - lr * scale * NS(M)
+    (Gram backend; see ns_muon_step in ns.h for the reading and the fusion)."""
+    if not (len(grads) == len(momenta) == len(params)):
+        raise ValueError("grads, momenta and params must have the same length")
+    if len(grads) == 0:
+        return
+    scales = [1.0] * len(grads) if scales is None else list(scales)
+    if len(scales) != len(grads):
+        raise ValueError("one scale per matrix")
+    mats = (_MuonMatrix * len(grads))()
+    for i, (G, M, W) in enumerate(zip(grads, momenta, params)):
+        for t, name in ((G, "grad"), (M, "momentum"), (W, "param")):
+            _device_tensor(t, name)
+            if tuple(t.shape) != tuple(G.shape):
+                raise ValueError(f"{name} {i} has shape {tuple(t.shape)}, grad {tuple(G.shape)}")
+        m, n = G.shape
+        mats[i] = _MuonMatrix(G.data_ptr(), _dtype_code(G.dtype), m, n, _rowmajor_ld(G),
+                              M.data_ptr(), _dtype_code(M.dtype), _rowmajor_ld(M),
+                              W.data_ptr(), _dtype_code(W.dtype), _rowmajor_ld(W),
+                              float(scales[i]))
+    p, keep = _params(coefficients, restart_iterations, eps)
+    lib = library()
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.ns_muon_workspace_size(mats, len(grads), ctypes.byref(p), ctypes.byref(nbytes)),
+           "ns_muon_workspace_size")
+    if workspace is None or workspace.numel() < nbytes.value:
+        workspace = _workspace(nbytes.value, grads[0].device)
+    _check(lib.ns_muon_step(mats, len(grads), ctypes.byref(p), float(beta), float(lr),
+                            workspace.data_ptr(), workspace.numel(), _stream_ptr(grads[0])),
+           "ns_muon_step")
 
 
 def ns_direct(G, coefficients=POLAR_EXPRESS_COEFFICIENTS, eps: float = DEFAULT_EPS,

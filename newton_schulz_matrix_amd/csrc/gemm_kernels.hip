@@ -216,7 +216,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 struct Epi {
   float alpha, beta, gamma, delta;
-  const _Float16* C;
+  const void* C;
+  int ldc, c_type;
   void* D;
   _Float16* D2;
   _Float16* DT;
@@ -229,6 +230,14 @@ struct Epi {
 // row-pair layout.
 __device__ __forceinline__ int64_t lidx(int pairs, int64_t i, int64_t j, int64_t ld) {
   return pairs ? pair_index(i, j, ld) : i * ld + j;
+}
+
+// C[i][j] as fp32, any element type.
+__device__ __forceinline__ float load_c(const Epi& e, int64_t i, int64_t j) {
+  const int64_t k = lidx(e.c_pairs, i, j, e.ldc);
+  if (e.c_type == OUT_F16) return static_cast<float>(gmem(static_cast<const _Float16*>(e.C))[k]);
+  if (e.c_type == OUT_F32) return gmem(static_cast<const float*>(e.C))[k];
+  return __uint_as_float(static_cast<uint32_t>(gmem(static_cast<const uint16_t*>(e.C))[k]) << 16);
 }
 
 // MFMA 32x32 output layout: register r of lane l holds row
@@ -247,7 +256,10 @@ __device__ __forceinline__ void epi_values(const floatx16& a, const Epi& e, int 
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     float x = e.alpha * a[G * 4 + q];
-    if (e.C) x += e.beta * static_cast<float>(gmem(e.C)[lidx(e.c_pairs, rb + q, col, e.N)]);
+    // C is read only where D is stored: a caller's C (row-major, its own
+    // leading dimension) ends at the real (valid_m, valid_n) block, while
+    // the tile covers the zero-padded size.
+    if (e.C && rb + q < e.valid_m && col < e.valid_n) x += e.beta * load_c(e, rb + q, col);
     if (rb + q == col && col < e.diag_n) x += e.gamma;
     v[q] = x;
   }
@@ -343,7 +355,7 @@ __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Flo
         if constexpr (SYM) {
           if (e.C) {
             const u32x4 cv = *gmem(reinterpret_cast<const u32x4*>(
-                e.C + lidx(e.c_pairs, col, rbase + 8 * (g0 + h), e.N)));
+                static_cast<const _Float16*>(e.C) + lidx(e.c_pairs, col, rbase + 8 * (g0 + h), e.ldc)));
             uint32_t x0 = cv[0], x1 = cv[1], y0 = cv[2], y1 = cv[3];
             lane_swap(x0, y0);
             lane_swap(x1, y1);
@@ -364,7 +376,8 @@ __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Flo
             float x = e.alpha * a[g * 4 + q];
             if constexpr (SYM) x += e.beta * c[GG][q];
             if constexpr (MODE == EPI_FULL_C)
-              x += e.beta * static_cast<float>(gmem(e.C)[lidx(e.c_pairs, row, col, e.N)]);
+              x += e.beta * static_cast<float>(
+                  gmem(static_cast<const _Float16*>(e.C))[lidx(e.c_pairs, row, col, e.ldc)]);
             v[q] = x;
           }
           if (bdiag) {
@@ -627,6 +640,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   Epi e;
   e.alpha = d.alpha; e.beta = d.beta; e.gamma = d.gamma; e.delta = d.delta;
   e.C = fold ? nullptr : d.C;   // folded C is already in the accumulators
+  e.ldc = d.ldc; e.c_type = d.c_type;
   e.D = d.D; e.D2 = d.D2; e.DT = d.DT;
   e.M = M; e.N = N; e.ldd = d.ldd; e.diag_n = d.diag_n;
   e.valid_m = d.valid_m; e.valid_n = d.valid_n; e.out_type = d.out_type;
@@ -647,7 +661,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
       epilogue_tile<C, EPI_SYM_DIAG>(acc, e, smem, sdiag, lane, wm, wn, m0, n0, nullptr, 0,
                                      nullptr);
   } else if (d.out_type == OUT_F16 && d.valid_m == M && d.valid_n == N && row_store_ok &&
-             !d.D2) {
+             !d.D2 && (!e.C || d.c_type == OUT_F16)) {
     if (e.C)
       epilogue_tile<C, EPI_FULL_C>(acc, e, smem, sdiag, lane, wm, wn, m0, n0, d.DT, M, nullptr);
     else

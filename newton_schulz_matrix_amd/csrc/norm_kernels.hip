@@ -21,32 +21,31 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Load 8 consecutive elements of row `row` starting at column `col` as fp32.
+// Load 8 consecutive elements (row `row`, columns col .. col+7) of a
+// row-major matrix of type `type`, m x n, leading dimension ld, as fp32.
 // Elements outside [0, m) x [0, n) read as 0.
-__device__ __forceinline__ void load8(const NormDesc& d, bool vec_ok, int row,
-                                      int col, float (&v)[8]) {
-  if (row >= d.m) {
+__device__ __forceinline__ void load8p(const void* base, int type, int64_t ld, int m, int n,
+                                       bool vec_ok, int row, int col, float (&v)[8]) {
+  if (row >= m) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = 0.f;
     return;
   }
-  const int64_t off = static_cast<int64_t>(row) * d.ldg + col;
-  if (vec_ok && col + 8 <= d.n) {
-    if (d.g_type == OUT_F32) {
-      const float4* p = reinterpret_cast<const float4*>(
-          static_cast<const float*>(d.G) + off);
+  const int64_t off = static_cast<int64_t>(row) * ld + col;
+  if (vec_ok && col + 8 <= n) {
+    if (type == OUT_F32) {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
       const float4 a = p[0], b = p[1];
       v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
       v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     } else {
-      const uint4 q = *reinterpret_cast<const uint4*>(
-          static_cast<const uint16_t*>(d.G) + off);
+      const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
       const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint16_t lo = static_cast<uint16_t>(w[e] & 0xffffu);
         const uint16_t hi = static_cast<uint16_t>(w[e] >> 16);
-        if (d.g_type == OUT_BF16) {
+        if (type == OUT_BF16) {
           v[2 * e] = bf16_to_f32(lo);
           v[2 * e + 1] = bf16_to_f32(hi);
         } else {
@@ -61,16 +60,51 @@ __device__ __forceinline__ void load8(const NormDesc& d, bool vec_ok, int row,
   for (int e = 0; e < 8; ++e) {
     const int c = col + e;
     float x = 0.f;
-    if (c < d.n) {
-      if (d.g_type == OUT_F32) {
-        x = static_cast<const float*>(d.G)[off + e];
+    if (c < n) {
+      if (type == OUT_F32) {
+        x = static_cast<const float*>(base)[off + e];
       } else {
-        const uint16_t b = static_cast<const uint16_t*>(d.G)[off + e];
-        x = d.g_type == OUT_BF16 ? bf16_to_f32(b)
-                                 : static_cast<float>(__builtin_bit_cast(_Float16, b));
+        const uint16_t b = static_cast<const uint16_t*>(base)[off + e];
+        x = type == OUT_BF16 ? bf16_to_f32(b)
+                             : static_cast<float>(__builtin_bit_cast(_Float16, b));
       }
     }
     v[e] = x;
+  }
+}
+
+__device__ __forceinline__ void load8(const NormDesc& d, bool vec_ok, int row, int col,
+                                      float (&v)[8]) {
+  load8p(d.G, d.g_type, d.ldg, d.m, d.n, vec_ok, row, col, v);
+}
+
+// Round to the storage type (nearest even) and back to fp32.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Store 8 fp32 values to row `row`, columns col .. col+7 (clipped to
+// [0, m) x [0, n)) of a row-major matrix of type `type`, rounding each to
+// nearest even; v is replaced by the stored (rounded) values.
+__device__ __forceinline__ void store8p(void* base, int type, int64_t ld, int m, int n,
+                                        int row, int col, float (&v)[8]) {
+  const int64_t off = static_cast<int64_t>(row) * ld + col;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (type == OUT_F32) continue;
+    if (type == OUT_BF16) v[e] = bf16_to_f32(f32_to_bf16_bits(v[e]));
+    else v[e] = static_cast<float>(static_cast<_Float16>(v[e]));
+  }
+  if (row >= m) return;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (col + e >= n) continue;
+    if (type == OUT_F32) static_cast<float*>(base)[off + e] = v[e];
+    else if (type == OUT_BF16) static_cast<uint16_t*>(base)[off + e] = f32_to_bf16_bits(v[e]);
+    else static_cast<_Float16*>(base)[off + e] = static_cast<_Float16>(v[e]);
   }
 }
 
@@ -115,12 +149,30 @@ __global__ __launch_bounds__(256) void sumsq_kernel(const NormDesc* __restrict__
   const int row0 = cr * SQ_ROWS + (threadIdx.x >> 5);
   const bool vec = vector_ok(d);
   float acc = 0.f;
+  if (!d.grad) {
 #pragma unroll
-  for (int q = 0; q < SQ_ROWS / 8; ++q) {
-    float v[8];
-    load8(d, vec, row0 + 8 * q, col, v);
+    for (int q = 0; q < SQ_ROWS / 8; ++q) {
+      float v[8];
+      load8(d, vec, row0 + 8 * q, col, v);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf(v[e], v[e], acc);
+      for (int e = 0; e < 8; ++e) acc = fmaf(v[e], v[e], acc);
+    }
+  } else {
+    // momentum step: each element read and written by this thread only
+    const int ge = d.grad_type == OUT_F32 ? 4 : 2;
+    const bool gvec = (reinterpret_cast<uintptr_t>(d.grad) % 16 == 0) && (d.ldgrad % (16 / ge) == 0);
+#pragma unroll
+    for (int q = 0; q < SQ_ROWS / 8; ++q) {
+      const int row = row0 + 8 * q;
+      float v[8], g[8];
+      load8(d, vec, row, col, v);
+      load8p(d.grad, d.grad_type, d.ldgrad, d.m, d.n, gvec, row, col, g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = fmaf(d.beta, v[e], g[e]);
+      store8p(const_cast<void*>(d.G), d.g_type, d.ldg, d.m, d.n, row, col, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf(v[e], v[e], acc);
+    }
   }
   const float s = block_sum256(acc, red);
   if (threadIdx.x == 0) d.partials[d.chunk_begin + c] = s;

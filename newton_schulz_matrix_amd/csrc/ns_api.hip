@@ -162,8 +162,9 @@ struct Stage {
 struct Probs {
   std::vector<GemmDesc> d;
   double flops = 0.0;
-  void add(GemmDesc g, double f, bool user_output = false) {
-    g.a_pairs = g.b_pairs = g.c_pairs = 1;
+  void add(GemmDesc g, double f, bool user_output = false, bool user_c = false) {
+    g.a_pairs = g.b_pairs = 1;
+    g.c_pairs = user_c ? 0 : 1;
     g.d_pairs = user_output ? 0 : 1;
     d.push_back(g);
     flops += f;
@@ -190,6 +191,10 @@ struct MatBuf {   // per-matrix workspace offsets (bytes from ws base)
 };
 
 struct Plan {
+  // Muon step (optional): per matrix the gradient added into the momentum
+  // in the norm pass, and the update fused into the final product.
+  const ns_muon_matrix* muon = nullptr;
+  float beta = 0.f, lr = 0.f;
   std::vector<MatBuf> mats;
   std::vector<int> order;          // matrices, largest first
   size_t partials_off = 0, norms_off = 0, table_off = 0, total = 0;
@@ -327,6 +332,8 @@ GemmDesc gemm(const _Float16* A, const _Float16* B, const _Float16* C, void* D,
   d.A = A; d.B = B; d.C = C; d.D = D; d.D2 = D2; d.DT = DT;
   d.M = static_cast<int>(M); d.N = static_cast<int>(N); d.K = static_cast<int>(K);
   d.ldd = static_cast<int>(ldd);
+  d.ldc = static_cast<int>(N);
+  d.c_type = OUT_F16;
   d.valid_m = static_cast<int>(valid_m); d.valid_n = static_cast<int>(valid_n);
   d.diag_n = static_cast<int>(diag_n);
   d.out_type = out_type;
@@ -376,6 +383,13 @@ void norm_stages(Builder& B, const ns_matrix* mats, float eps) {
     d.n = static_cast<int>(b.n);
     d.eps = eps;
     d.pairs = 1;
+    if (pl.muon) {   // M <- beta M + grad in the norm pass
+      const ns_muon_matrix& u = pl.muon[i];
+      d.grad = u.grad;
+      d.ldgrad = u.ld_grad;
+      d.grad_type = out_code(u.grad_dtype);
+      d.beta = pl.beta;
+    }
     d.norm_out = nullptr;
     d.norm_slot = reinterpret_cast<float*>(B.ws + pl.norms_off) + i;
     d.partials = reinterpret_cast<float*>(B.ws + pl.partials_off);
@@ -426,6 +440,25 @@ void final_output(Builder& B, const ns_matrix& mt, const MatBuf& b, const Shard&
   // (tall) of the caller's output.
   const int ot = out_code(mt.out_dtype);
   const double f = gen_flops(b.s, h.lc, b.s);
+  const Plan& pl = B.pl;
+  if (pl.muon) {
+    // Muon update fused into the epilogue: W <- W - lr * scale * (Q X),
+    // W (the caller's buffer, row-major) is both C and D.
+    const ns_muon_matrix& u = pl.muon[&b - pl.mats.data()];
+    const float alpha = -pl.lr * u.scale;
+    const size_t st = elem_bytes(u.param_dtype) * (b.tall ? static_cast<size_t>(u.ld_param) : 1);
+    void* w = u.param ? static_cast<unsigned char*>(u.param) + static_cast<size_t>(h.c0) * st
+                      : nullptr;
+    GemmDesc g = !b.tall ? gemm(Qm, XT, nullptr, w, nullptr, nullptr, b.Sp, h.Lp, b.Sp,
+                                u.ld_param, b.m, h.lc, 0, ot, false, alpha, 1.f, 0.f, 0.f)
+                         : gemm(XT, Qm, nullptr, w, nullptr, nullptr, h.Lp, b.Sp, b.Sp,
+                                u.ld_param, h.lc, b.n, 0, ot, false, alpha, 1.f, 0.f, 0.f);
+    g.C = w;
+    g.ldc = static_cast<int>(u.ld_param);
+    g.c_type = ot;
+    out.add(g, f, true, true);
+    return;
+  }
   const size_t step = elem_bytes(mt.out_dtype) * (b.tall ? static_cast<size_t>(mt.ldo) : 1);
   void* o = mt.out ? static_cast<unsigned char*>(mt.out) + static_cast<size_t>(h.c0) * step
                    : nullptr;
@@ -590,7 +623,11 @@ void direct_stages(Builder& B, const ns_matrix* mats, const ns_params& p) {
 }
 
 ns_status build_plan(Plan& pl, const ns_matrix* mats, int count, ns_backend be,
-                     const ns_params& p, unsigned char* ws, int shards = 1) {
+                     const ns_params& p, unsigned char* ws, int shards = 1,
+                     const ns_muon_matrix* muon = nullptr, float beta = 0.f, float lr = 0.f) {
+  pl.muon = muon;
+  pl.beta = beta;
+  pl.lr = lr;
   layout(pl, mats, count, be, shards);
   Builder B(pl, ws);
   if (be == NS_GRAM) gram_stages(B, mats, p);
@@ -706,17 +743,18 @@ ns_status check_shards(const ns_matrix& a, int shards) {
 }
 
 ns_status run_batched(const ns_matrix* mats, int count, ns_backend be, const ns_params* p,
-                      void* ws, size_t ws_bytes, void* stream, int shards = 1) {
+                      void* ws, size_t ws_bytes, void* stream, int shards = 1,
+                      const ns_muon_matrix* muon = nullptr, float beta = 0.f, float lr = 0.f) {
   ns_status s = check_call(mats, count, be, p);
   if (s != NS_OK) return s;
   if (count == 0) return NS_OK;
   Plan sizing;
-  build_plan(sizing, mats, count, be, *p, nullptr, shards);
+  build_plan(sizing, mats, count, be, *p, nullptr, shards, muon, beta, lr);
   if (!ws || ws_bytes < sizing.total) return NS_ERR_WORKSPACE;
   s = check_device();
   if (s != NS_OK) return s;
   Plan pl;
-  build_plan(pl, mats, count, be, *p, static_cast<unsigned char*>(ws), shards);
+  build_plan(pl, mats, count, be, *p, static_cast<unsigned char*>(ws), shards, muon, beta, lr);
   return run_plan(pl, static_cast<unsigned char*>(ws), static_cast<hipStream_t>(stream));
 }
 
@@ -872,6 +910,59 @@ NS_API ns_status ns_gram_sharded(const ns_matrix* mat, int shards, const ns_para
   ns_status s = check_shards(*mat, shards);
   if (s != NS_OK) return s;
   return run_batched(mat, 1, NS_GRAM, params, ws, ws_bytes, stream, shards);
+}
+
+// Muon step: the momentum buffer is the NS input (g), the parameter the
+// output; the gradient and scale ride along in the plan.
+namespace nsmi {
+namespace {
+ns_status muon_matrices(const ns_muon_matrix* mats, int count, float beta, float lr,
+                        std::vector<ns_matrix>& out, bool need_pointers) {
+  if (count < 0 || (count > 0 && !mats)) return NS_ERR_INVALID_ARG;
+  if (!std::isfinite(beta) || !std::isfinite(lr)) return NS_ERR_INVALID_ARG;
+  out.resize(count);
+  for (int i = 0; i < count; ++i) {
+    const ns_muon_matrix& u = mats[i];
+    if (!dtype_ok(u.grad_dtype) || u.ld_grad < u.n || u.ld_momentum < u.n ||
+        !std::isfinite(u.scale))
+      return NS_ERR_INVALID_ARG;
+    if (need_pointers && (!u.grad || !u.momentum || !u.param)) return NS_ERR_INVALID_ARG;
+    ns_matrix& a = out[i];
+    a.g = u.momentum;
+    a.g_dtype = u.momentum_dtype;
+    a.m = u.m;
+    a.n = u.n;
+    a.ldg = u.ld_momentum;
+    a.out = u.param;
+    a.out_dtype = u.param_dtype;
+    a.ldo = u.ld_param;
+    ns_status s = need_pointers ? check_matrix(a) : check_matrix_shape(a);
+    if (s != NS_OK) return s;
+  }
+  return NS_OK;
+}
+}  // namespace
+}  // namespace nsmi
+
+NS_API ns_status ns_muon_workspace_size(const ns_muon_matrix* mats, int count,
+                                        const ns_params* params, size_t* bytes) {
+  if (!bytes || count < 1) return NS_ERR_INVALID_ARG;
+  std::vector<ns_matrix> m;
+  ns_status s = muon_matrices(mats, count, 0.f, 0.f, m, false);
+  if (s == NS_OK) s = check_params(params, NS_GRAM);
+  if (s != NS_OK) return s;
+  Plan pl;
+  build_plan(pl, m.data(), count, NS_GRAM, *params, nullptr, 1, mats, 0.f, 0.f);
+  *bytes = pl.total;
+  return NS_OK;
+}
+
+NS_API ns_status ns_muon_step(const ns_muon_matrix* mats, int count, const ns_params* params,
+                              float beta, float lr, void* ws, size_t ws_bytes, void* stream) {
+  std::vector<ns_matrix> m;
+  ns_status s = muon_matrices(mats, count, beta, lr, m, true);
+  if (s != NS_OK) return s;
+  return run_batched(m.data(), count, NS_GRAM, params, ws, ws_bytes, stream, 1, mats, beta, lr);
 }
 
 NS_API ns_status ns_direct(const ns_matrix* mat, const ns_params* params, void* ws,

@@ -34,7 +34,9 @@ __host__ __device__ inline int64_t pair_index(int64_t i, int64_t j, int64_t ld) 
 //   D[i][j]  = v                       (dtype out_type, leading dim ldd)
 //   D2[i][j] = v + (i == j && i < diag_n ? delta : 0)      (fp16, ld N)
 //   DT[j][i] = v                       (fp16, transposed, leading dim M)
-// Stores to D are clipped to i < valid_m, j < valid_n.
+// C[i][j] is read with leading dimension ldc and element type c_type
+// (fp16 for every internal buffer; a caller's C of any type takes the
+// general epilogue). Stores to D are clipped to i < valid_m, j < valid_n.
 // Layouts: a_pairs / b_pairs / c_pairs select the row-pair layout (leading
 // dimension K for A and B, N for C) instead of row-major; d_pairs does the
 // same for D (ld ldd), D2 (ld N) and DT (ld M).
@@ -47,12 +49,14 @@ __host__ __device__ inline int64_t pair_index(int64_t i, int64_t j, int64_t ld) 
 struct GemmDesc {
   const _Float16* A;
   const _Float16* B;
-  const _Float16* C;   // may alias D (same element read then written)
+  const void* C;       // may alias D (same element read then written)
   void* D;
   _Float16* D2;        // optional
   _Float16* DT;        // optional
   int M, N, K;
   int ldd;
+  int ldc;             // leading dimension of C (N for internal buffers)
+  int c_type;          // OUT_F16 for internal buffers; any OutType for a caller's C
   int valid_m, valid_n;
   int diag_n;
   int out_type;
@@ -82,6 +86,14 @@ struct NormDesc {
   int64_t ldpt;
   int pairs;
   float eps;
+  // Momentum update fused into the sum-of-squares pass (Muon step): when
+  // grad is set, G is the momentum buffer M and the pass first stores
+  // M <- fp(beta * M + grad) (fp32 fma, rounded to M's type), then sums the
+  // squares of the stored values; the cast pass reads the updated M.
+  const void* grad;
+  int64_t ldgrad;
+  int grad_type;
+  float beta;
   float* norm_out;     // optional copy of the norm (device)
   float* norm_slot;    // where the finalize kernel stores the norm
   float* partials;     // chunk partial sums of squares

@@ -25,6 +25,7 @@ from .ns_oracle import (  # noqa: F401
     gram_newton_schulz,
     gram_newton_schulz_sharded,
     shard_bounds,
+    muon_step,
     closed_form,
     scalar_map,
     step_maps,

@@ -41,6 +41,10 @@ iteration (X split by columns, R as the sum of per-shard Gram matrices,
 per-shard restarts and outputs): the pages' exact-TP statement in section
 "Gram 空间 NS", and section "6. 与TP的结合" of the distributed-Muon article.
 
+``muon_step`` composes the momentum update, the Gram iteration and the
+parameter update along a stated reading of the article page's description
+(its formula is missing from the pages): parity unpinned as to the pages.
+
 Parity pins (tests/test_oracle_pins.py): gram == direct in fp64, the SVD
 closed form ``closed_form`` (singular values mapped by the composed scalar
 polynomial, singular vectors kept), restart invariance, and special cases
@@ -206,6 +210,30 @@ def gram_newton_schulz_sharded(G, coefficients=POLAR_EXPRESS_COEFFICIENTS,
             R = M @ R @ M
     out = np.concatenate([Q @ Xi for Xi in Xs], axis=1)
     return out.T.copy() if transposed else out
+
+
+def muon_step(G, M, W, beta: float, lr: float, scale: float = 1.0,
+              coefficients=POLAR_EXPRESS_COEFFICIENTS,
+              restart_iterations=DEFAULT_RESTARTS, eps: float = DEFAULT_EPS):
+    """One Muon step around the Gram iteration, in fp64: returns (M', W').
+
+    PARITY UNPINNED against the pages: the article page (sections
+    "1. Introduction" and "2. Muon执行过程") says only that a Muon step keeps
+    a momentum M of the gradient, orthogonalises M and uses the result as
+    the update direction; the formula itself is missing from the extracted
+    text and no beta or update scale is given (lr = 0.02 appears in an
+    example). This function is the plainest reading of that description:
+
+        M' = beta M + G,    W' = W - lr * scale * gram_newton_schulz(M').
+
+    What is pinned (tests/test_oracle_muon.py) is this composition: the
+    momentum recursion against its geometric closed form, the update
+    against the SVD closed form of M', and linearity in lr * scale.
+    """
+    G, M, W = _as_f64(G), _as_f64(M), _as_f64(W)
+    M_new = beta * M + G
+    O = gram_newton_schulz(M_new, coefficients, restart_iterations, eps)
+    return M_new, W - (lr * scale) * O
 
 
 def step_maps(coefficients):

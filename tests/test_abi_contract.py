@@ -246,3 +246,43 @@ def test_sharded_call_rejects_bad_arguments_before_any_device_work():
         == nsmi.NS_ERR_WORKSPACE
     assert lib.ns_gram_sharded(_mats([(16, 32)], None, fake), 2, ctypes.byref(p), fake,
                                1 << 30, None) == nsmi.NS_ERR_INVALID_ARG
+
+
+def _muon(shapes, g=None, m=None, w=None, scale=1.0, dt=None):
+    dt = nsmi.NS_DT_F32 if dt is None else dt
+    arr = (nsmi._MuonMatrix * len(shapes))()
+    for i, (r, c) in enumerate(shapes):
+        arr[i] = nsmi._MuonMatrix(g, dt, r, c, c, m, dt, c, w, dt, c, scale)
+    return arr
+
+
+def test_muon_workspace_matches_the_gram_layout():
+    lib = nsmi.library()
+    p, keep = _params()
+    shapes = [(256, 1024), (1024, 256), (300, 700)]
+    nb = ctypes.c_size_t(0)
+    assert lib.ns_muon_workspace_size(_muon(shapes), 3, ctypes.byref(p), ctypes.byref(nb)) \
+        == nsmi.NS_OK
+    assert nb.value == _size(shapes)
+
+
+def test_muon_step_rejects_bad_arguments_before_any_device_work():
+    lib = nsmi.library()
+    p, keep = _params()
+    fake = 0x1000
+    ok = _muon([(16, 32)], fake, fake, fake)
+    call = lambda mats, beta=0.9, lr=0.02, n=1, ws=1 << 30: lib.ns_muon_step(
+        mats, n, ctypes.byref(p), beta, lr, fake, ws, None)
+    assert call(_muon([(16, 32)], None, fake, fake)) == nsmi.NS_ERR_INVALID_ARG
+    assert call(_muon([(16, 32)], fake, None, fake)) == nsmi.NS_ERR_INVALID_ARG
+    assert call(_muon([(16, 32)], fake, fake, None)) == nsmi.NS_ERR_INVALID_ARG
+    assert call(_muon([(16, 32)], fake, fake, fake, dt=9)) == nsmi.NS_ERR_INVALID_ARG
+    assert call(_muon([(16, 32)], fake, fake, fake, scale=float("nan"))) == nsmi.NS_ERR_INVALID_ARG
+    assert call(ok, beta=float("inf")) == nsmi.NS_ERR_INVALID_ARG
+    assert call(ok, lr=float("nan")) == nsmi.NS_ERR_INVALID_ARG
+    assert call(ok, n=-1) == nsmi.NS_ERR_INVALID_ARG
+    assert call(ok, ws=16) == nsmi.NS_ERR_WORKSPACE
+    assert lib.ns_muon_step(None, 0, ctypes.byref(p), 0.9, 0.02, None, 0, None) == nsmi.NS_OK
+    bad_ld = _muon([(16, 32)], fake, fake, fake)
+    bad_ld[0].ld_grad = 8
+    assert call(bad_ld) == nsmi.NS_ERR_INVALID_ARG

@@ -1,0 +1,115 @@
+"""GPU checks of the fused Muon step (ns_muon_step) against the oracle's
+reading of it (oracle.muon_step; its formula is a reading, the pages' is
+missing, so parity against the pages is unpinned, and the composition is
+pinned in tests/test_oracle_muon.py).
+
+* momentum: M' = fp(beta M + G) from one fp32 fma per element: within one
+  ulp of the fp64 value rounded to M's type (bitwise in >= 99.9% of
+  elements for fp32);
+* parameter: the applied update (W' - W) / (-lr scale) against the oracle
+  NS of M' at the 1e-2 bar (fp32 parameters, so W's rounding is far below
+  the update); bf16 buffers within their rounding;
+* a batch of mixed shapes equals per-matrix calls bitwise, lr = 0 leaves W
+  bitwise unchanged, beta = 0 gives M' = G, several steps accumulate.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import newton_schulz_matrix_amd as nsmi
+import workloads as W
+from gpu_helpers import rel_fro, require_gpu, to64
+from oracle import YOU_COEFFICIENTS, muon_step
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(shape, seed, dt=torch.float32):
+    G = W.small_gaussian(seed, *shape)
+    M = W.small_gaussian(seed + 100, *shape)
+    P = W.small_gaussian(seed + 200, *shape) * 0.02
+    return G.to(dt), M.to(dt), P.to(dt)
+
+
+def _ulps32(a, b):
+    ia = a.astype(np.float32).view(np.int32).astype(np.int64)
+    ib = b.astype(np.float32).view(np.int32).astype(np.int64)
+    return np.abs(ia - ib)
+
+
+@pytest.mark.parametrize("shape", [(300, 1000), (1000, 300), (256, 256), (7, 13)])
+def test_muon_step_fp32(shape):
+    require_gpu()
+    G, M, P = _case(shape, sum(shape))
+    beta, lr, scale = 0.95, 0.02, 1.5
+    g, m, p = G.cuda(), M.cuda(), P.cuda()
+    nsmi.ns_muon_step([g], [m], [p], beta, lr, [scale], nsmi.YOU_COEFFICIENTS, (2,))
+    torch.cuda.synchronize()
+    M1, P1 = muon_step(to64(G), to64(M), to64(P), np.float64(np.float32(beta)), lr, scale,
+                       YOU_COEFFICIENTS, (2,))
+    u = _ulps32(m.cpu().numpy(), M1)
+    assert u.max() <= 1 and np.mean(u == 0) >= 0.999
+    upd = (to64(p) - to64(P)) / (-np.float64(np.float32(lr)) * np.float64(np.float32(scale)))
+    want = (P1 - to64(P)) / (-lr * scale)
+    err = rel_fro(upd, want)
+    print(f"muon {shape}: update rel err {err:.3e}", flush=True)
+    assert err <= 1e-2
+
+
+def test_muon_step_bf16_buffers():
+    require_gpu()
+    G, M, P = _case((384, 1000), 5, torch.bfloat16)
+    beta, lr = 0.9, 0.02
+    g, m, p = G.cuda(), M.cuda(), P.cuda()
+    nsmi.ns_muon_step([g], [m], [p], beta, lr, None, nsmi.YOU_COEFFICIENTS, (2,))
+    torch.cuda.synchronize()
+    M1, P1 = muon_step(to64(G), to64(M), to64(P), np.float64(np.float32(beta)), lr, 1.0,
+                       YOU_COEFFICIENTS, (2,))
+    # momentum: one bf16 rounding of the fp32 fma
+    want_m = torch.from_numpy(M1).float().to(torch.bfloat16).double().numpy()
+    ulp_m = np.maximum(np.abs(want_m), 1e-30) * 2.0 ** -7
+    assert np.all(np.abs(to64(m) - want_m) <= ulp_m)
+    # parameter: one bf16 rounding after the update, which the oracle NS drives
+    ulp_p = np.maximum(np.abs(P1), 1e-30) * 2.0 ** -7
+    upd_err = lr * np.abs(P1 - to64(P)).max() / lr * 0.05
+    assert np.all(np.abs(to64(p) - P1) <= ulp_p + upd_err)
+
+
+def test_muon_batched_equals_single_calls_and_edge_cases():
+    require_gpu()
+    shapes = [(300, 1000), (1000, 300), (256, 700), (64, 64)]
+    cases = [_case(s, 40 + i) for i, s in enumerate(shapes)]
+    scales = [1.0, 0.5, 2.0, 1.25]
+    gs = [c[0].cuda() for c in cases]
+    ms = [c[1].cuda() for c in cases]
+    ps = [c[2].cuda() for c in cases]
+    nsmi.ns_muon_step(gs, ms, ps, 0.9, 0.02, scales, nsmi.YOU_COEFFICIENTS, (2,))
+    for i, c in enumerate(cases):
+        m1, p1 = c[1].cuda(), c[2].cuda()
+        nsmi.ns_muon_step([gs[i]], [m1], [p1], 0.9, 0.02, [scales[i]], nsmi.YOU_COEFFICIENTS,
+                          (2,))
+        torch.cuda.synchronize()
+        assert torch.equal(m1, ms[i]) and torch.equal(p1, ps[i])
+    # lr = 0: parameters untouched; beta = 0: momentum becomes the gradient
+    G, M, P = _case((300, 700), 77)
+    g, m, p = G.cuda(), M.cuda(), P.cuda()
+    nsmi.ns_muon_step([g], [m], [p], 0.0, 0.0, None, nsmi.YOU_COEFFICIENTS, (2,))
+    torch.cuda.synchronize()
+    assert torch.equal(p.cpu(), P) and torch.equal(m.cpu(), G)
+
+
+def test_muon_three_steps():
+    require_gpu()
+    G, M, P = _case((512, 1500), 9)
+    g, m, p = G.cuda(), M.cuda(), P.cuda()
+    M64, P64 = to64(M), to64(P)
+    for _ in range(3):
+        nsmi.ns_muon_step([g], [m], [p], 0.9, 0.02, None, nsmi.YOU_COEFFICIENTS, (2,))
+        M64, P64 = muon_step(to64(G), M64, P64, np.float64(np.float32(0.9)), 0.02, 1.0,
+                             YOU_COEFFICIENTS, (2,))
+    torch.cuda.synchronize()
+    assert rel_fro(to64(m), M64) < 1e-6
+    err = rel_fro(to64(p) - to64(P), P64 - to64(P))
+    print(f"three steps: accumulated update rel err {err:.3e}", flush=True)
+    assert err <= 1e-2
