@@ -45,7 +45,8 @@ def parse():
     ap.add_argument("--backend", choices=["gram", "direct"], default="gram",
                     help="headline backend")
     ap.add_argument("--no-second-backend", action="store_true",
-                    help="time only the headline backend")
+                    help="time only the headline backend (also skips the Muon-step and "
+                         "sharded-route lines)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=25.0,
                     help="seconds of oracle work for the CPU baseline sample")
@@ -115,6 +116,40 @@ def time_backend(nsmi, torch, Gs, outs, backend, table, restarts, steps, warmup)
     ms = start.elapsed_time(end) / steps
     del ws
     return {"ms_per_step": ms, "wall_s": wall, "timing": rep}
+
+
+def time_muon(nsmi, torch, Gs, table, restarts, steps):
+    """Fused Muon step on the same batch: bf16 gradients, fp32 momentum and
+    parameters (updated in place), beta 0.95, lr 0.02, scale 1."""
+    Ms = [torch.zeros(G.shape, dtype=torch.float32, device="cuda") for G in Gs]
+    Ps = [torch.full(G.shape, 0.01, dtype=torch.float32, device="cuda") for G in Gs]
+    nsmi.ns_muon_step(Gs, Ms, Ps, 0.95, 0.02, None, table, restarts)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        nsmi.ns_muon_step(Gs, Ms, Ps, 0.95, 0.02, None, table, restarts)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def time_sharded(nsmi, torch, G, table, restarts, shards, steps):
+    """One matrix along the column-sharded route with `shards` virtual
+    shards, against the unsharded call."""
+    res = {}
+    for name, fn in (("unsharded", lambda: nsmi.ns_gram(G, table, restarts)),
+                     ("sharded", lambda: nsmi.ns_gram_sharded(G, shards, table, restarts))):
+        fn()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(steps):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        res[name] = start.elapsed_time(end) / steps
+    return res
 
 
 def cpu_baseline(workload, restarts, budget_s):
@@ -271,6 +306,23 @@ def main():
             "ms_per_step": r["ms_per_step"], "steps": r["steps"],
             "matrices_per_s": n / (r["ms_per_step"] * 1e-3),
             "tflops": tt["gemm_flops"] / r["steps"] / (r["ms_per_step"] * 1e-3) / 1e12}
+    if not args.no_second_backend and args.backend == "gram":
+        mu = time_muon(nsmi, torch, Gs, table, restarts, 3)
+        out["muon_step"] = {
+            "ms_per_step": mu, "ns_ms_per_step": ms,
+            "overhead_pct": 100.0 * (mu - ms) / ms,
+            "config": "ns_muon_step on the same 28 matrices: bf16 gradients, fp32 momentum "
+                      "and parameters, beta 0.95, lr 0.02 (momentum fused into the norm "
+                      "pass, update into the final product)"}
+        log(f"muon step: {mu:.3f} ms/step ({out['muon_step']['overhead_pct']:+.1f}% vs NS)")
+        gate = next(G for G in Gs if tuple(G.shape) == (14336, 4096))
+        sh = time_sharded(nsmi, torch, gate, table, restarts, 4, 5)
+        out["tp_emulation"] = {
+            "matrix": "gate projection 14336 x 4096 (bf16)", "shards": 4,
+            "ms_sharded": sh["sharded"], "ms_unsharded": sh["unsharded"],
+            "note": "ns_gram_sharded: 4 virtual column shards on one GPU; the shard "
+                    "reduction stands in for the all-reduce"}
+        log(f"tp emulation (4 shards, gate): {sh['sharded']:.3f} ms vs {sh['unsharded']:.3f} ms")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, restarts, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -194,16 +194,6 @@ __device__ __forceinline__ const NSMI_GLOBAL T* gmem(const T* p) {
   return (const NSMI_GLOBAL T*)(p);
 }
 
-__device__ __forceinline__ void store_out(void* D, int out_type, int64_t idx, float v) {
-  if (out_type == OUT_F16) {
-    gmem(static_cast<_Float16*>(D))[idx] = static_cast<_Float16>(v);
-  } else if (out_type == OUT_F32) {
-    gmem(static_cast<float*>(D))[idx] = v;
-  } else {
-    gmem(static_cast<uint16_t*>(D))[idx] = to_bf16_bits(v);
-  }
-}
-
 // Compile-time loop: f(integral_constant<int, I>) for I in [B, E). Keeps
 // accumulator indices constant so the accumulators stay in registers.
 template <int B, int E, class F>
@@ -232,59 +222,74 @@ __device__ __forceinline__ int64_t lidx(int pairs, int64_t i, int64_t j, int64_t
   return pairs ? pair_index(i, j, ld) : i * ld + j;
 }
 
-// C[i][j] as fp32, any element type.
-__device__ __forceinline__ float load_c(const Epi& e, int64_t i, int64_t j) {
-  const int64_t k = lidx(e.c_pairs, i, j, e.ldc);
-  if (e.c_type == OUT_F16) return static_cast<float>(gmem(static_cast<const _Float16*>(e.C))[k]);
-  if (e.c_type == OUT_F32) return gmem(static_cast<const float*>(e.C))[k];
-  return __uint_as_float(static_cast<uint32_t>(gmem(static_cast<const uint16_t*>(e.C))[k]) << 16);
+// Typed element access for the general epilogue (type fixed at compile time).
+template <int T>
+__device__ __forceinline__ float load_typed(const void* p, int64_t k) {
+  if constexpr (T == OUT_F16) return static_cast<float>(gmem(static_cast<const _Float16*>(p))[k]);
+  else if constexpr (T == OUT_F32) return gmem(static_cast<const float*>(p))[k];
+  else return __uint_as_float(static_cast<uint32_t>(gmem(static_cast<const uint16_t*>(p))[k]) << 16);
+}
+template <int T>
+__device__ __forceinline__ void store_typed(void* p, int64_t k, float v) {
+  if constexpr (T == OUT_F16) gmem(static_cast<_Float16*>(p))[k] = static_cast<_Float16>(v);
+  else if constexpr (T == OUT_F32) gmem(static_cast<float*>(p))[k] = v;
+  else gmem(static_cast<uint16_t*>(p))[k] = to_bf16_bits(v);
 }
 
 // MFMA 32x32 output layout: register r of lane l holds row
-// 8*(r/4) + 4*(l/32) + r%4 and column l%32 of each 32x32 block. For block
-// (I, J) and register group g this lane owns rows rb .. rb+3 of column col.
-template <class Cf, int I, int J, int G>
-__device__ __forceinline__ void block_coords(const Epi& e, int& rb, int& col) {
-  rb = e.row0 + I * 32 + G * 8;
-  col = e.col0 + J * 32;
-}
+// 8*(r/4) + 4*(l/32) + r%4 and column l%32 of each 32x32 block.
 
-// v = alpha * acc + beta * C (+ gamma on the real diagonal), 4 rows.
-template <int G>
-__device__ __forceinline__ void epi_values(const floatx16& a, const Epi& e, int rb, int col,
-                                           float (&v)[4]) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float x = e.alpha * a[G * 4 + q];
-    // C is read only where D is stored: a caller's C (row-major, its own
-    // leading dimension) ends at the real (valid_m, valid_n) block, while
-    // the tile covers the zero-padded size.
-    if (e.C && rb + q < e.valid_m && col < e.valid_n) x += e.beta * load_c(e, rb + q, col);
-    if (rb + q == col && col < e.diag_n) x += e.gamma;
-    v[q] = x;
-  }
-}
-
-// Scalar epilogue for general products whose output is not an fp16 internal
-// buffer: user buffer, dtype fp16 / bf16 / fp32, clipped to the real
-// (valid_m, valid_n) block (no second output).
-template <class Cf, class Acc>
-__device__ __forceinline__ void epilogue_output(const Acc& acc, const Epi& e) {
+// General epilogue for outputs that are not fp16 internal buffers: a
+// caller's buffer of any type, clipped to the real (valid_m, valid_n)
+// block, with an optional C of any type (read only inside that block; it
+// may be the output itself). Types are template parameters, and each
+// block's C values are loaded together before any is used, so one memory
+// latency is paid per block rather than per element.
+//   v = alpha * acc + beta * C + (gamma on the real diagonal)
+template <class Cf, int OT, int CT, class Acc>
+__device__ __forceinline__ void epilogue_output_t(const Acc& acc, const Epi& e) {
   static_for<0, Cf::FM>([&](auto I) {
     static_for<0, Cf::FN>([&](auto J) {
       const floatx16& a = acc[I][J];
-      static_for<0, 4>([&](auto G) {
-        int rb, col;
-        block_coords<Cf, I, J, G>(e, rb, col);
-        float v[4];
-        epi_values<G>(a, e, rb, col, v);
+      const int col = e.col0 + J * 32;
+      const int rb0 = e.row0 + I * 32;
+      const bool col_ok = col < e.valid_n;
+      float c[16];
+      if constexpr (CT >= 0) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (rb + q < e.valid_m && col < e.valid_n)
-            store_out(e.D, e.out_type, lidx(e.d_pairs, rb + q, col, e.ldd), v[q]);
-      });
+        for (int r = 0; r < 16; ++r) {
+          const int row = rb0 + (r / 4) * 8 + (r % 4);
+          c[r] = (col_ok && row < e.valid_m)
+                     ? load_typed<CT>(e.C, lidx(e.c_pairs, row, col, e.ldc)) : 0.f;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rb0 + (r / 4) * 8 + (r % 4);
+        float x = e.alpha * a[r];
+        if constexpr (CT >= 0) x += e.beta * c[r];
+        if (row == col && col < e.diag_n) x += e.gamma;
+        if (col_ok && row < e.valid_m) store_typed<OT>(e.D, lidx(e.d_pairs, row, col, e.ldd), x);
+      }
     });
   });
+}
+
+template <class Cf, class Acc>
+__device__ __forceinline__ void epilogue_output(const Acc& acc, const Epi& e) {
+  const int ct = e.C ? e.c_type : -1;
+#define NSMI_EPI_OUT(OT)                                                            \
+  if (e.out_type == OT) {                                                          \
+    if (ct == OUT_F16) epilogue_output_t<Cf, OT, OUT_F16>(acc, e);                \
+    else if (ct == OUT_F32) epilogue_output_t<Cf, OT, OUT_F32>(acc, e);           \
+    else if (ct == OUT_BF16) epilogue_output_t<Cf, OT, OUT_BF16>(acc, e);         \
+    else epilogue_output_t<Cf, OT, -1>(acc, e);                                    \
+    return;                                                                        \
+  }
+  NSMI_EPI_OUT(OUT_F16)
+  NSMI_EPI_OUT(OUT_F32)
+  NSMI_EPI_OUT(OUT_BF16)
+#undef NSMI_EPI_OUT
 }
 
 // ------------------------------------------------------------------ fast epilogue

@@ -90,15 +90,34 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
 // [0, m) x [0, n)) of a row-major matrix of type `type`, rounding each to
 // nearest even; v is replaced by the stored (rounded) values.
 __device__ __forceinline__ void store8p(void* base, int type, int64_t ld, int m, int n,
-                                        int row, int col, float (&v)[8]) {
+                                        bool vec_ok, int row, int col, float (&v)[8]) {
   const int64_t off = static_cast<int64_t>(row) * ld + col;
+  uint16_t bits[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     if (type == OUT_F32) continue;
-    if (type == OUT_BF16) v[e] = bf16_to_f32(f32_to_bf16_bits(v[e]));
-    else v[e] = static_cast<float>(static_cast<_Float16>(v[e]));
+    if (type == OUT_BF16) {
+      bits[e] = f32_to_bf16_bits(v[e]);
+      v[e] = bf16_to_f32(bits[e]);
+    } else {
+      const _Float16 hv = static_cast<_Float16>(v[e]);
+      bits[e] = __builtin_bit_cast(uint16_t, hv);
+      v[e] = static_cast<float>(hv);
+    }
   }
   if (row >= m) return;
+  if (vec_ok && col + 8 <= n) {   // 16-byte aligned row piece
+    if (type == OUT_F32) {
+      float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + off);
+      p[0] = make_float4(v[0], v[1], v[2], v[3]);
+      p[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+      uint4 w;
+      __builtin_memcpy(&w, bits, 16);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off) = w;
+    }
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     if (col + e >= n) continue;
@@ -169,7 +188,7 @@ __global__ __launch_bounds__(256) void sumsq_kernel(const NormDesc* __restrict__
       load8p(d.grad, d.grad_type, d.ldgrad, d.m, d.n, gvec, row, col, g);
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = fmaf(d.beta, v[e], g[e]);
-      store8p(const_cast<void*>(d.G), d.g_type, d.ldg, d.m, d.n, row, col, v);
+      store8p(const_cast<void*>(d.G), d.g_type, d.ldg, d.m, d.n, vec, row, col, v);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc = fmaf(v[e], v[e], acc);
     }
