@@ -319,26 +319,43 @@ __device__ __forceinline__ void lane_swap(uint32_t& x, uint32_t& y) {
   y = r[1];
 }
 
-// Output staging: the whole 256 x 256 fp16 tile, row-major, 16-byte chunks
-// XOR-swizzled by f(row) = 8 (row & 1) + 4 ((row >> 2) & 1): the two rows a
-// register store covers (r and r+4) and the two rows 16 lanes read back
-// (r and r+1) fall on different banks.
-__device__ __forceinline__ int tile_idx(int row, int col) {
-  const int f = ((row & 1) << 3) | (((row >> 2) & 1) << 2);
-  return row * 256 + ((((col >> 3) ^ f)) << 3) + (col & 7);
+// Output staging: the tile transposed. Tile column c is the 512-byte LDS
+// row c; its 16-byte chunk k holds tile rows 8k..8k+7 and sits at physical
+// chunk k ^ stage_sw(c). Both access patterns spread over the 16 bank groups:
+// a staging write (32 consecutive columns, two chunks each) and a transposing
+// read (16 columns: 4 per 16-lane group, at column offsets 0-3, 8-11, 16-19,
+// 24-27 or their +4 shifts).
+__device__ __forceinline__ int stage_sw(int c) { return (c & 31) ^ (((c >> 4) & 1) << 2); }
+__device__ __forceinline__ uint32_t stage_off(int c, int chunk) {
+  return static_cast<uint32_t>(c) * 512u + (static_cast<uint32_t>(chunk ^ stage_sw(c)) << 4);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane j supplies the address
+// of four consecutive 16-bit values M[j][0..3]; lane i receives
+// M[4q + i/4][i%4] in slot q.
+__device__ __forceinline__ u32x2 lds_read_tr(const lds_char* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
 }
 
 enum EpiMode { EPI_SYM_OFFDIAG, EPI_SYM_DIAG, EPI_FULL, EPI_FULL_C };
 
 // Fast epilogue for fp16 outputs inside internal (padded, aligned) buffers:
 //   * v = alpha acc + beta C + gamma (real diagonal) in fp32, rounded once;
-//   * row-major stores staged through LDS, 16 bytes per lane;
-//   * transposed stores (symmetric mirror, or DT) from registers after a
-//     32-lane swap, 16 bytes per lane;
+//   * a 32-lane swap gives each lane eight consecutive rows of one column
+//     (16 bytes): stored as is for the transposed outputs (symmetric mirror,
+//     or DT), and staged in LDS for the row-major output;
+//   * row-major stores read the staging with transposing LDS reads, so each
+//     lane stores eight consecutive columns of one row (16 bytes);
 //   * symmetric C read from its transpose in 16-byte chunks;
-//   * diagonal tiles: elements on/below the diagonal are staged at (r, c)
-//     and (c, r), so the tile comes out exactly symmetric; the second output
-//     D2 = D + delta I takes delta on the fp32 diagonal value.
+//   * diagonal tiles: elements above the diagonal take the value computed
+//     at the mirrored position, so the tile comes out exactly symmetric; the
+//     second output D2 = D + delta I takes delta on the fp32 diagonal value.
 template <class Cf, int MODE, class Acc>
 __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Float16* S,
                                               float* sdiag, int lane, int wm, int wn,
@@ -346,6 +363,7 @@ __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Flo
                                               _Float16* T2) {
   static_assert(Cf::BM == 256 && Cf::BN == 256, "tile-wide staging is 256 x 256");
   constexpr bool SYM = MODE == EPI_SYM_OFFDIAG || MODE == EPI_SYM_DIAG;
+  lds_char* const Sl = (lds_char*)(S);
   const int h = lane >> 5;
   static_for<0, Cf::FM>([&](auto I) {
     static_for<0, Cf::FN>([&](auto J) {
@@ -370,8 +388,7 @@ __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Flo
         }
         // The diagonal term exists only in 32 x 32 blocks on the diagonal;
         // the test is uniform, so other blocks skip the per-element compare.
-        const bool bdiag = MODE != EPI_SYM_OFFDIAG && e.gamma != 0.f &&
-                           rbase == col - (lane & 31) && rbase < e.diag_n;
+        const bool bdiag = MODE != EPI_SYM_OFFDIAG && rbase == col - (lane & 31);
         static_for<0, 2>([&](auto GG) {
           constexpr int g = g0 + GG;
           float v[4];
@@ -389,70 +406,79 @@ __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Flo
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const int row = rbase + g * 8 + h * 4 + q;
-              if (row == col && col < e.diag_n) v[q] += e.gamma;
+              if (e.gamma != 0.f && row == col && col < e.diag_n) v[q] += e.gamma;
+              if constexpr (MODE == EPI_SYM_DIAG)
+                if (row == col) sdiag[row - m0] = v[q];
             }
           }
           P[g][0] = pack_h2(v[0], v[1]);
           P[g][1] = pack_h2(v[2], v[3]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int lr = lrow0 + g * 8 + h * 4 + q;
-            const uint32_t w = P[g][q >> 1];
-            const _Float16 hv =
-                __builtin_bit_cast(_Float16, static_cast<uint16_t>((q & 1) ? (w >> 16) : (w & 0xffffu)));
-            if constexpr (MODE == EPI_SYM_DIAG) {
-              if (lr >= lcol) {
-                S[tile_idx(lr, lcol)] = hv;
-                if (lr != lcol) S[tile_idx(lcol, lr)] = hv;
-                else sdiag[lr] = v[q];
-              }
-            } else {
-              S[tile_idx(lr, lcol)] = hv;
-            }
-          }
         });
-      });
-      if constexpr (MODE != EPI_SYM_DIAG) {
-        if (T) {   // transposed copy: 8 consecutive rows per lane after the swap
-          static_for<0, 2>([&](auto GP) {
-            constexpr int g0 = 2 * GP;
-            uint32_t x0 = P[g0][0], x1 = P[g0][1], y0 = P[g0 + 1][0], y1 = P[g0 + 1][1];
-            lane_swap(x0, y0);
-            lane_swap(x1, y1);
-            const u32x4 out = {x0, x1, y0, y1};
+        // eight consecutive rows of column `col` per lane: rows
+        // rbase + 8 (g0 + h) .. + 7
+        uint32_t x0 = P[g0][0], x1 = P[g0][1], y0 = P[g0 + 1][0], y1 = P[g0 + 1][1];
+        lane_swap(x0, y0);
+        lane_swap(x1, y1);
+        const u32x4 out = {x0, x1, y0, y1};
+        *(__attribute__((address_space(3))) u32x4*)(Sl + stage_off(lcol, (lrow0 >> 3) + g0 + h)) = out;
+        if constexpr (MODE != EPI_SYM_DIAG) {
+          if (T) {   // transposed copy
             const int64_t off = lidx(e.d_pairs, col, rbase + 8 * (g0 + h), ldT);
             *gmem(reinterpret_cast<u32x4*>(T + off)) = out;
             if (T2) *gmem(reinterpret_cast<u32x4*>(T2 + off)) = out;
-          });
+          }
         }
-      }
+      });
     });
   });
   // Diagonal tiles mirror across waves: wait for every wave's staging.
+  // Otherwise each wave reads back only what it staged itself.
   if constexpr (MODE == EPI_SYM_DIAG) __syncthreads();
-  // Row-major copy of this wave's 128 x 64 block: 16 bytes per lane.
+  // Row-major copy of this wave's 128 x 64 block, 16 rows x 32 columns per
+  // instruction: 16-lane group gq covers columns 8 gq .. 8 gq + 7, lane j of
+  // it one row. Source lane j = 4 q + a of a transposing read points at tile
+  // rows 4a .. 4a + 3 of column q (+4 for the second read).
   _Float16* D = static_cast<_Float16*>(e.D);
-#pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    const int id = it * 64 + lane;
-    const int lr = wm * Cf::WM + (id >> 3), lc = wn * Cf::WN + (id & 7) * 8;
-    u32x4 val = *reinterpret_cast<const u32x4*>(&S[tile_idx(lr, lc)]);
-    const int64_t off = lidx(e.d_pairs, m0 + lr, n0 + lc, e.ldd);
-    *gmem(reinterpret_cast<u32x4*>(D + off)) = val;
-    if (e.D2) {
+  const int gq = lane >> 4, j = lane & 15, qa = j >> 2, aa = j & 3;
+  static_for<0, Cf::WM / 16>([&](auto RB) {
+    static_for<0, Cf::WN / 32>([&](auto CB) {
+      const int R0 = wm * Cf::WM + RB * 16, C0 = wn * Cf::WN + CB * 32;
+      const int chunk = (R0 >> 3) + (aa >> 1);
+      const int c1 = C0 + 8 * gq + qa;
+      const u32x2 t1 = lds_read_tr(Sl + stage_off(c1, chunk) + (aa & 1) * 8);
+      const u32x2 t2 = lds_read_tr(Sl + stage_off(c1 + 4, chunk) + (aa & 1) * 8);
+      u32x4 val = {t1[0], t1[1], t2[0], t2[1]};
+      const int lr = R0 + j, lc = C0 + 8 * gq;   // this lane's row, first column
       if constexpr (MODE == EPI_SYM_DIAG) {
-        // the second output adds delta on the real diagonal, from fp32
-        if (lr >= lc && lr < lc + 8 && m0 + lr < e.diag_n) {
-          const int k = lr - lc;
-          const uint16_t hb = __builtin_bit_cast(uint16_t, static_cast<_Float16>(sdiag[lr] + e.delta));
-          const uint32_t w = val[k >> 1];
-          val[k >> 1] = (k & 1) ? ((w & 0xffffu) | (static_cast<uint32_t>(hb) << 16))
-                                : ((w & 0xffff0000u) | hb);
+        // column lc + k lies above the diagonal iff k > lr - lc: take the
+        // value computed at (lc + k, lr), i.e. chunk lc / 8 of column lr
+        const int dd = lr - lc;
+        if (dd < 7) {
+          const u32x4 up = *(const __attribute__((address_space(3))) u32x4*)(Sl + stage_off(lr, lc >> 3));
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t m = (2 * w > dd ? 0x0000ffffu : 0u) | (2 * w + 1 > dd ? 0xffff0000u : 0u);
+            val[w] = (val[w] & ~m) | (up[w] & m);
+          }
         }
       }
-      *gmem(reinterpret_cast<u32x4*>(e.D2 + lidx(e.d_pairs, m0 + lr, n0 + lc, e.N))) = val;
-    }
-  }
+      const int64_t off = lidx(e.d_pairs, m0 + lr, n0 + lc, e.ldd);
+      *gmem(reinterpret_cast<u32x4*>(D + off)) = val;
+      if (e.D2) {
+        if constexpr (MODE == EPI_SYM_DIAG) {
+          // the second output adds delta on the real diagonal, from fp32
+          if (lr >= lc && lr < lc + 8 && m0 + lr < e.diag_n) {
+            const int k = lr - lc;
+            const uint16_t hb = __builtin_bit_cast(uint16_t, static_cast<_Float16>(sdiag[lr] + e.delta));
+            const uint32_t w = val[k >> 1];
+            val[k >> 1] = (k & 1) ? ((w & 0xffffu) | (static_cast<uint32_t>(hb) << 16))
+                                  : ((w & 0xffff0000u) | hb);
+          }
+        }
+        *gmem(reinterpret_cast<u32x4*>(e.D2 + lidx(e.d_pairs, m0 + lr, n0 + lc, e.N))) = val;
+      }
+    });
+  });
 }
 
 template <class C>
