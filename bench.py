@@ -39,7 +39,7 @@ METRIC = "NS matrices/s + TFLOP/s (% fp16 MFMA peak), Llama-8B owner batch"
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--backend", choices=["gram", "direct"], default="gram",
@@ -102,20 +102,24 @@ def time_backend(nsmi, torch, Gs, outs, backend, table, restarts, steps, warmup)
     torch.cuda.synchronize()
     nsmi.ns_timing_enable(True)
     nsmi.ns_timing_read()  # clear
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps: the block total gives ms_per_step,
+    # the per-step spans their median
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record()
-    for _ in range(steps):
+    evs[0].record()
+    for i in range(steps):
         nsmi.ns_batched(Gs, backend, table, restarts, outs=outs, workspace=ws)
-    end.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     nsmi.ns_timing_enable(False)
     rep = nsmi.ns_timing_read()
-    ms = start.elapsed_time(end) / steps
+    ms = evs[0].elapsed_time(evs[-1]) / steps
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    median = (per[(steps - 1) // 2] + per[steps // 2]) / 2
     del ws
-    return {"ms_per_step": ms, "wall_s": wall, "timing": rep}
+    return {"ms_per_step": ms, "median_ms_per_step": median, "wall_s": wall, "timing": rep}
 
 
 def time_muon(nsmi, torch, Gs, table, restarts, steps):
@@ -271,6 +275,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "median_ms_per_step": head["median_ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
