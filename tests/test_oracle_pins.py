@@ -157,6 +157,40 @@ def test_rank_one(backend, shape):
 
 
 @pytest.mark.parametrize("backend", [direct_newton_schulz, gram_newton_schulz])
+def test_rank_one_polar_express_diverges(backend):
+    """Frobenius normalisation puts the only singular value of a rank-one
+    input at 1 (up to eps). The page's Polar Express table maps 1 to
+    7.893 - 20.381 + 14.939 = 2.451 and the later steps grow it without
+    bound (to ~3e131): the method diverges there, and the oracle must follow
+    the composed scalar map into that regime as well."""
+    rng = np.random.default_rng(5)
+    u, v = rng.standard_normal(40), rng.standard_normal(90)
+    G = np.outer(u, v)
+    nu = np.linalg.norm(u) * np.linalg.norm(v)
+    p = scalar_map(POLAR_EXPRESS_COEFFICIENTS, nu / (nu + 1e-7))
+    assert abs(scalar_map(POLAR_EXPRESS_COEFFICIENTS[:1], 1.0) - 2.451) < 1e-12
+    assert p > 1e100
+    want = p * np.outer(u / np.linalg.norm(u), v / np.linalg.norm(v))
+    assert rel(backend(G, POLAR_EXPRESS_COEFFICIENTS), want) < 1e-9
+
+
+@pytest.mark.parametrize("backend", [direct_newton_schulz, gram_newton_schulz])
+@pytest.mark.parametrize("table", ["polar_express", "you"])
+@pytest.mark.parametrize("shape,r", [((30, 70), 4), ((70, 30), 3), ((40, 40), 2)])
+def test_rank_deficient_null_space_stays_zero(backend, table, shape, r):
+    """G = U V^T with r orthonormal column pairs: ||G||_F = sqrt(r), so the
+    normalised singular values are 1/(sqrt(r) + eps) on span(U, V) and 0
+    elsewhere. Every step maps 0 to p_k(0) = 0, so the output is exactly
+    p(1/(sqrt(r) + eps)) U V^T."""
+    rng = np.random.default_rng(17 + r)
+    U = np.linalg.qr(rng.standard_normal((shape[0], r)))[0]
+    V = np.linalg.qr(rng.standard_normal((shape[1], r)))[0]
+    co = COEFFICIENT_SETS[table]
+    want = scalar_map(co, 1.0 / (np.sqrt(r) + 1e-7)) * (U @ V.T)
+    assert rel(backend(U @ V.T, co), want) < 1e-12
+
+
+@pytest.mark.parametrize("backend", [direct_newton_schulz, gram_newton_schulz])
 def test_zero_and_scalar(backend):
     assert not np.any(backend(np.zeros((4, 9)), POLAR_EXPRESS_COEFFICIENTS))
     for g in (2.5, -0.75):
