@@ -56,14 +56,10 @@ struct Cfg {
   static constexpr int THREADS = WAVES_M * WAVES_N * 64;
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int KCH = BK / 8;  // 16-byte chunks per tile row
-  static constexpr int A_LOADS = BM * KCH / THREADS;
-  static constexpr int B_LOADS = BN * KCH / THREADS;
   static constexpr int KSTEPS = BK / 16;
   static constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;
   static_assert(BM == BN, "square tiles (symmetric mode mirrors tiles)");
   static_assert(KCH == 4, "swizzle assumes 64-byte LDS rows");
-  static_assert(A_LOADS * THREADS == BM * KCH, "A tile / thread mismatch");
-  static_assert(B_LOADS * THREADS == BN * KCH, "B tile / thread mismatch");
 };
 
 // Workgroup tile 256 x 256, K slices of 32, eight waves of 128 x 64.
@@ -293,10 +289,10 @@ __device__ __forceinline__ void epilogue_output(const Acc& acc, const Epi& e) {
 }
 
 // ------------------------------------------------------------------ fast epilogue
-// Row-major stores go through a per-wave LDS staging area (the operand ring
-// is idle after the main loop) so that each lane stores 16 bytes; stores of
-// the transpose use a 32-lane swap so that each lane holds 8 consecutive
-// rows of one column (16 bytes).
+// After a 32-lane swap each lane holds 8 consecutive rows of one column (16
+// bytes): stored directly for transposed outputs, and staged in LDS (the
+// operand ring is idle after the main loop) for row-major ones, which read
+// it back transposed so that each lane again stores 16 bytes.
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
