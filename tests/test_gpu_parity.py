@@ -244,6 +244,30 @@ def test_bitwise_determinism():
 
 
 @pytest.mark.parametrize("backend", ["gram", "direct"])
+def test_many_matrices_one_call(backend):
+    """300 small matrices of mixed shape in one grouped call: descriptor
+    tables of that length, the per-tile problem search over them and tiles
+    of many problems in one launch. Every output is bitwise the per-matrix
+    call's; a sample is checked against the oracle."""
+    require_gpu()
+    rng = np.random.default_rng(77)
+    shapes = [(int(rng.integers(1, 300)), int(rng.integers(1, 300))) for _ in range(300)]
+    Gs = [W.small_gaussian(500 + i, *sh).cuda() for i, sh in enumerate(shapes)]
+    outs = nsmi.ns_batched(Gs, backend, nsmi.YOU_COEFFICIENTS, (2,))
+    torch.cuda.synchronize()
+    for i, (G, o) in enumerate(zip(Gs, outs)):
+        if backend == "gram":
+            single = nsmi.ns_gram(G, nsmi.YOU_COEFFICIENTS, (2,))
+        else:
+            single = nsmi.ns_direct(G, nsmi.YOU_COEFFICIENTS)
+        torch.cuda.synchronize()
+        assert torch.equal(o, single), (i, shapes[i])
+    for i in range(0, 300, 37):
+        err = rel_fro(to64(outs[i]), run_oracle(Gs[i].cpu(), backend, "you"))
+        assert err <= 1e-2, (i, shapes[i], err)
+
+
+@pytest.mark.parametrize("backend", ["gram", "direct"])
 def test_batched_equals_single_calls(backend):
     require_gpu()
     shapes = [(300, 700), (512, 256), (64, 64), (256, 1024), (1000, 300), (5, 9)]
