@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=25.0,
                     help="seconds of oracle work for the CPU baseline sample")
+    ap.add_argument("--only", choices=["muon", "sharded"], default=None,
+                    help="time only the Muon step on the batch, or only the 4-shard "
+                         "column-sharded route on its gate projection, for --steps "
+                         "steps (for profiling those paths), print one JSON line, exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run three plain device copies of BYTES bytes (reference "
                          "for the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -242,6 +246,18 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs: {len(Gs)} matrices generated in {time.perf_counter() - t0:.1f} s")
     outs = [torch.empty(G.shape, dtype=torch.float16, device="cuda") for G in Gs]
+    if args.only == "muon":
+        mu = time_muon(nsmi, torch, Gs, table, restarts, args.steps)
+        print(json.dumps({"only": "muon_step", "ms_per_step": mu, "steps": args.steps,
+                          "matrices": len(Gs)}), flush=True)
+        return
+    if args.only == "sharded":
+        gate = next(G for G in Gs if tuple(G.shape) == (14336, 4096))
+        sh = time_sharded(nsmi, torch, gate, table, restarts, 4, args.steps)
+        print(json.dumps({"only": "tp_emulation", "shards": 4, "steps": args.steps,
+                          "ms_sharded": sh["sharded"], "ms_unsharded": sh["unsharded"]}),
+              flush=True)
+        return
 
     backends = [args.backend]
     if not args.no_second_backend:
