@@ -1,0 +1,60 @@
+"""bench.py's contract, checked without a GPU.
+
+* --gpus N > 1 exits with a message and prints no result line;
+* with no GPU visible it fails loudly instead of printing a number;
+* the roofline `traffic` figure is read from the committed profile only
+  while the GEMM source is the one the counters were taken on;
+* the cpu_baseline object carries the keys the report needs.
+"""
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def run_bench(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                          capture_output=True, text=True, timeout=300)
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = run_bench("--gpus", "2")
+    assert r.returncode == 2
+    assert "exactly one GPU" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def test_no_gpu_fails_loudly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    r = run_bench("--steps", "1", "--warmup", "0", "--no-cpu-baseline")
+    assert r.returncode != 0
+    assert "needs a GPU" in (r.stdout + r.stderr)
+    assert not any(line.startswith("{") for line in r.stdout.splitlines())
+
+
+def test_traffic_only_for_the_profiled_source(tmp_path, monkeypatch):
+    v = bench.gemm_traffic_per_launch()
+    assert v is None or v > 0
+    changed = tmp_path / "gemm_kernels.hip"
+    changed.write_bytes(open(bench.GEMM_SRC, "rb").read() + b"\n// edited\n")
+    monkeypatch.setattr(bench, "GEMM_SRC", str(changed))
+    assert bench.gemm_traffic_per_launch() is None
+
+
+def test_cpu_baseline_keys():
+    out = bench.cpu_baseline(1, (2,), 1.0)      # the 256 x 1024 workload: a fraction of a second
+    for key in ("value", "unit", "cores", "kind", "sample"):
+        assert key in out
+    assert out["kind"] == "oracle" and out["unit"] == "matrices/s"
+    assert out["value"] > 0 and out["cores"] >= 1
+    json.dumps(out)
