@@ -247,17 +247,18 @@ ns_status ns_gemm_nt(const void* a, const void* b, const void* c, void* d,
                      void* stream);
 
 /* Kernel timing (measurement aid). While enabled, every launch made by
- * ns_normalize / ns_gram / ns_gram_sharded / ns_direct / ns_batched is
- * bracketed by two HIP
- * events on the caller's stream. ns_timing_read waits for the recorded
+ * ns_normalize / ns_gram / ns_gram_sharded / ns_direct / ns_batched /
+ * ns_muon_step is bracketed by two HIP events on the caller's stream. ns_timing_read waits for the recorded
  * events, reports the totals since the last read, and clears them. The
  * algorithmic work counts exclude zero padding:
  *   gemm_flops   2 m n k per general product; s (s + 1) k per symmetric
  *                product (SYRK and the Gram-space products);
  *   norm_bytes   HBM bytes the normalisation must move: the input read
  *                twice (norm pass, scale pass) and two fp16 copies written;
- *                the norm_* fields also count the shard reductions of
- *                ns_gram_sharded (every part read once, the sum written).
+ *                for ns_muon_step the momentum pass also reads the
+ *                gradient and writes the momentum; the norm_* fields also
+ *                count the shard reductions of ns_gram_sharded (every part
+ *                read once, the sum written).
  * Enabling or disabling is global to the process; disabled by default. */
 typedef struct {
   double gemm_ms;

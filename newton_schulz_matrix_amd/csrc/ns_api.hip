@@ -369,12 +369,14 @@ void norm_stages(Builder& B, const ns_matrix* mats, float eps) {
   Plan& pl = B.pl;
   std::vector<NormDesc> v, cast;
   int tile_begin = 0;
-  double read_bytes = 0.0, write_bytes = 0.0;
+  double read_bytes = 0.0, write_bytes = 0.0, momentum_bytes = 0.0;
   for (int i : pl.order) {
     const MatBuf& b = pl.mats[i];
     const double elems = double(b.m) * double(b.n);
     read_bytes += elems * elem_bytes(mats[i].g_dtype);
     write_bytes += elems * 2.0 * 2.0;
+    if (pl.muon)   // the momentum pass also reads the gradient and writes M
+      momentum_bytes += elems * (elem_bytes(pl.muon[i].grad_dtype) + elem_bytes(mats[i].g_dtype));
     NormDesc d{};
     d.G = mats[i].g;
     d.ldg = mats[i].ldg;
@@ -425,7 +427,7 @@ void norm_stages(Builder& B, const ns_matrix* mats, float eps) {
   std::vector<NormDesc> by_chunk = v;
   std::sort(by_chunk.begin(), by_chunk.end(),
             [](const NormDesc& a, const NormDesc& b) { return a.chunk_begin < b.chunk_begin; });
-  B.push(Stage::SUMSQ, by_chunk, pl.total_chunks, read_bytes);
+  B.push(Stage::SUMSQ, by_chunk, pl.total_chunks, read_bytes + momentum_bytes);
   B.push(Stage::FINALIZE, v, static_cast<int>(v.size()), 0.0);
   B.push(Stage::CAST, cast, tile_begin, read_bytes + write_bytes);
 }
