@@ -220,16 +220,27 @@ def _dtype_code(dtype) -> int:
 
 
 def _rowmajor_ld(t) -> int:
+    """Leading dimension of a row-major 2-D view. Rows must be contiguous and
+    must not overlap (an expanded or otherwise aliased view would make the
+    library read or write past the storage it covers)."""
     if t.dim() != 2:
         raise ValueError("expected a 2-D tensor")
     if t.stride(1) != 1 and t.shape[1] > 1:
         raise ValueError("rows must be contiguous (stride(1) == 1)")
-    return max(t.stride(0), t.shape[1]) if t.shape[0] > 1 else t.shape[1]
+    if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+        raise ValueError(f"row stride {t.stride(0)} is smaller than the row length "
+                         f"{t.shape[1]} (overlapping rows, e.g. an expanded view)")
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
 
 
 def _device_tensor(t, name: str):
+    """A tensor on the current HIP device (where the library launches)."""
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    cur = _torch().cuda.current_device()
+    if t.device.index != cur:
+        raise ValueError(f"{name} is on {t.device} but the current device is cuda:{cur}; "
+                         f"the library runs on the current device")
     return t
 
 

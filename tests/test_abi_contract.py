@@ -286,3 +286,23 @@ def test_muon_step_rejects_bad_arguments_before_any_device_work():
     bad_ld = _muon([(16, 32)], fake, fake, fake)
     bad_ld[0].ld_grad = 8
     assert call(bad_ld) == nsmi.NS_ERR_INVALID_ARG
+
+
+def test_binding_leading_dimension_rules():
+    """Row-major views only: contiguous rows that do not overlap. An
+    expanded (stride-0) or transposed view is refused before any pointer
+    reaches the library; column slices keep their row stride as ld."""
+    import torch
+    base = torch.zeros(6, 10)
+    assert nsmi._rowmajor_ld(base) == 10
+    assert nsmi._rowmajor_ld(base[:, 2:7]) == 10          # column slice: ld = row stride
+    assert nsmi._rowmajor_ld(base[:1]) == 10              # one row
+    assert nsmi._rowmajor_ld(torch.zeros(1, 10).expand(1, 10)) == 10
+    with pytest.raises(ValueError, match="overlapping rows"):
+        nsmi._rowmajor_ld(torch.zeros(1, 10).expand(5, 10))
+    with pytest.raises(ValueError, match="overlapping rows"):
+        nsmi._rowmajor_ld(torch.zeros(40).as_strided((4, 10), (5, 1)))
+    with pytest.raises(ValueError, match="contiguous"):
+        nsmi._rowmajor_ld(base.t())
+    with pytest.raises(ValueError, match="2-D"):
+        nsmi._rowmajor_ld(torch.zeros(2, 3, 4))
