@@ -31,8 +31,10 @@
  *   Streams     `stream` is a hipStream_t passed as void* (NULL = the null
  *               stream). Calls enqueue work and return; results are valid
  *               once the stream reaches them. Outputs must not overlap
- *               inputs or the workspace. Concurrent calls on different
- *               streams need different workspaces.
+ *               inputs or the workspace; a matrix whose output range
+ *               overlaps its own input range is refused (NS_ERR_INVALID_ARG),
+ *               other overlaps are the caller's to avoid. Concurrent calls on
+ *               different streams need different workspaces.
  *   Errors      Return codes only: nothing is printed and nothing is thrown.
  *               Argument checks run on the host before any device work; on
  *               any error other than NS_ERR_HIP nothing has been enqueued.

@@ -140,9 +140,25 @@ ns_status check_matrix_shape(const ns_matrix& a) {
   return NS_OK;
 }
 
+// Byte range [first, last) a row-major (rows, cols, ld) matrix of `es`-byte
+// elements spans from `p`.
+struct Span { uintptr_t first, last; };
+Span span(const void* p, int64_t rows, int64_t cols, int64_t ld, size_t es) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return {a, a + (static_cast<uintptr_t>(rows - 1) * ld + cols) * es};
+}
+bool overlap(Span x, Span y) { return x.first < y.last && y.first < x.last; }
+
 ns_status check_matrix(const ns_matrix& a) {
   if (!a.g || !a.out) return NS_ERR_INVALID_ARG;
-  return check_matrix_shape(a);
+  const ns_status s = check_matrix_shape(a);
+  if (s != NS_OK) return s;
+  // the output must not overlap the input (the input is read again after
+  // outputs of other matrices of the call have been written)
+  const size_t gi = a.g_dtype == NS_DT_F32 ? 4 : 2, oi = a.out_dtype == NS_DT_F32 ? 4 : 2;
+  if (overlap(span(a.g, a.m, a.n, a.ldg, gi), span(a.out, a.m, a.n, a.ldo, oi)))
+    return NS_ERR_INVALID_ARG;
+  return NS_OK;
 }
 
 // ----------------------------------------------------------------- planning

@@ -121,18 +121,19 @@ def test_calls_reject_bad_arguments_before_any_device_work():
     lib = nsmi.library()
     p, keep = _params()
     fake = 0x1000
-    good = _mats([(16, 32)], fake, fake)
+    fake_out, fake_m, fake_w = 0x100000, 0x200000, 0x300000   # distinct, never touched
+    good = _mats([(16, 32)], fake, fake_out)
     # null matrix pointers
     assert lib.ns_gram(_mats([(16, 32)], None, fake), ctypes.byref(p), fake, 1 << 30, None) \
         == nsmi.NS_ERR_INVALID_ARG
     assert lib.ns_direct(_mats([(16, 32)], fake, None), ctypes.byref(p), fake, 1 << 30, None) \
         == nsmi.NS_ERR_INVALID_ARG
     # leading dimension smaller than n
-    bad_ld = _mats([(16, 32)], fake, fake)
+    bad_ld = _mats([(16, 32)], fake, fake_out)
     bad_ld[0].ldg = 8
     assert lib.ns_gram(bad_ld, ctypes.byref(p), fake, 1 << 30, None) == nsmi.NS_ERR_INVALID_ARG
     # bad dtype
-    bad_dt = _mats([(16, 32)], fake, fake)
+    bad_dt = _mats([(16, 32)], fake, fake_out)
     bad_dt[0].out_dtype = 7
     assert lib.ns_gram(bad_dt, ctypes.byref(p), fake, 1 << 30, None) == nsmi.NS_ERR_INVALID_ARG
     # bad backend / negative count
@@ -155,6 +156,7 @@ def test_calls_reject_bad_arguments_before_any_device_work():
 def test_normalize_and_unit_calls_reject_bad_arguments():
     lib = nsmi.library()
     fake = 0x1000
+    fake_out, fake_m, fake_w = 0x100000, 0x200000, 0x300000   # distinct, never touched
     nb = ctypes.c_size_t(0)
     assert lib.ns_normalize_workspace_size(3, 5, ctypes.byref(nb)) == nsmi.NS_OK and nb.value > 0
     assert lib.ns_normalize_workspace_size(0, 5, ctypes.byref(nb)) == nsmi.NS_ERR_INVALID_ARG
@@ -194,7 +196,8 @@ def test_valid_call_without_device_reports_unsupported():
     lib = nsmi.library()
     p, keep = _params()
     fake = 0x1000
-    good = _mats([(16, 32)], fake, fake)
+    fake_out, fake_m, fake_w = 0x100000, 0x200000, 0x300000   # distinct, never touched
+    good = _mats([(16, 32)], fake, fake_out)
     assert lib.ns_gram(good, ctypes.byref(p), fake, 1 << 40, None) == nsmi.NS_ERR_UNSUPPORTED
     assert lib.ns_normalize(fake, 0, 3, 5, 5, fake, 5, 1, 1e-7, None, fake, 1 << 20, None) \
         == nsmi.NS_ERR_UNSUPPORTED
@@ -235,7 +238,8 @@ def test_sharded_call_rejects_bad_arguments_before_any_device_work():
     lib = nsmi.library()
     p, keep = _params()
     fake = 0x1000
-    good = _mats([(16, 32)], fake, fake)
+    fake_out, fake_m, fake_w = 0x100000, 0x200000, 0x300000   # distinct, never touched
+    good = _mats([(16, 32)], fake, fake_out)
     assert lib.ns_gram_sharded(None, 2, ctypes.byref(p), fake, 1 << 30, None) \
         == nsmi.NS_ERR_INVALID_ARG
     assert lib.ns_gram_sharded(good, 0, ctypes.byref(p), fake, 1 << 30, None) \
@@ -270,20 +274,21 @@ def test_muon_step_rejects_bad_arguments_before_any_device_work():
     lib = nsmi.library()
     p, keep = _params()
     fake = 0x1000
-    ok = _muon([(16, 32)], fake, fake, fake)
+    fake_out, fake_m, fake_w = 0x100000, 0x200000, 0x300000   # distinct, never touched
+    ok = _muon([(16, 32)], fake, fake_m, fake_w)
     call = lambda mats, beta=0.9, lr=0.02, n=1, ws=1 << 30: lib.ns_muon_step(
         mats, n, ctypes.byref(p), beta, lr, fake, ws, None)
-    assert call(_muon([(16, 32)], None, fake, fake)) == nsmi.NS_ERR_INVALID_ARG
-    assert call(_muon([(16, 32)], fake, None, fake)) == nsmi.NS_ERR_INVALID_ARG
-    assert call(_muon([(16, 32)], fake, fake, None)) == nsmi.NS_ERR_INVALID_ARG
-    assert call(_muon([(16, 32)], fake, fake, fake, dt=9)) == nsmi.NS_ERR_INVALID_ARG
-    assert call(_muon([(16, 32)], fake, fake, fake, scale=float("nan"))) == nsmi.NS_ERR_INVALID_ARG
+    assert call(_muon([(16, 32)], None, fake_m, fake_w)) == nsmi.NS_ERR_INVALID_ARG
+    assert call(_muon([(16, 32)], fake, None, fake_w)) == nsmi.NS_ERR_INVALID_ARG
+    assert call(_muon([(16, 32)], fake, fake_m, None)) == nsmi.NS_ERR_INVALID_ARG
+    assert call(_muon([(16, 32)], fake, fake_m, fake_w, dt=9)) == nsmi.NS_ERR_INVALID_ARG
+    assert call(_muon([(16, 32)], fake, fake_m, fake_w, scale=float("nan"))) == nsmi.NS_ERR_INVALID_ARG
     assert call(ok, beta=float("inf")) == nsmi.NS_ERR_INVALID_ARG
     assert call(ok, lr=float("nan")) == nsmi.NS_ERR_INVALID_ARG
     assert call(ok, n=-1) == nsmi.NS_ERR_INVALID_ARG
     assert call(ok, ws=16) == nsmi.NS_ERR_WORKSPACE
     assert lib.ns_muon_step(None, 0, ctypes.byref(p), 0.9, 0.02, None, 0, None) == nsmi.NS_OK
-    bad_ld = _muon([(16, 32)], fake, fake, fake)
+    bad_ld = _muon([(16, 32)], fake, fake_m, fake_w)
     bad_ld[0].ld_grad = 8
     assert call(bad_ld) == nsmi.NS_ERR_INVALID_ARG
 
@@ -306,3 +311,19 @@ def test_binding_leading_dimension_rules():
         nsmi._rowmajor_ld(base.t())
     with pytest.raises(ValueError, match="2-D"):
         nsmi._rowmajor_ld(torch.zeros(2, 3, 4))
+
+
+def test_output_overlapping_its_input_is_refused():
+    """A matrix whose output byte range overlaps its input range is refused
+    on the host, before any device work (pointers are never dereferenced)."""
+    lib = nsmi.library()
+    p, _keep = nsmi._params(nsmi.POLAR_EXPRESS_COEFFICIENTS, (2,), 1e-7)
+    base = 1 << 40                                    # a fake, never-touched address
+    for out_off in (0, 8 * 2 - 2, 7 * 16 * 2):        # same start, inside row 0, last row
+        m = nsmi._Matrix(base, nsmi.NS_DT_F16, 8, 16, 16, base + out_off, nsmi.NS_DT_F16, 16)
+        assert lib.ns_batched(ctypes.byref(m), 1, nsmi.NS_GRAM, ctypes.byref(p), ctypes.c_void_p(1),
+                              1 << 30, None) == nsmi.NS_ERR_INVALID_ARG
+    # just past the input's last byte: passes argument checks (no GPU here)
+    m = nsmi._Matrix(base, nsmi.NS_DT_F16, 8, 16, 16, base + 8 * 16 * 2, nsmi.NS_DT_F16, 16)
+    assert lib.ns_batched(ctypes.byref(m), 1, nsmi.NS_GRAM, ctypes.byref(p), ctypes.c_void_p(1),
+                          1 << 30, None) in (nsmi.NS_ERR_UNSUPPORTED, nsmi.NS_OK)
