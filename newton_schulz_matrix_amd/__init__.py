@@ -261,6 +261,9 @@ def _params(coefficients, restart_iterations, eps):
 
 
 def _matrix(G, out) -> _Matrix:
+    if tuple(out.shape) != tuple(G.shape):
+        raise ValueError(f"output shape {tuple(out.shape)} differs from input shape "
+                         f"{tuple(G.shape)}")
     return _Matrix(G.data_ptr(), _dtype_code(G.dtype), G.shape[0], G.shape[1],
                    _rowmajor_ld(G), out.data_ptr(), _dtype_code(out.dtype),
                    _rowmajor_ld(out))
@@ -441,6 +444,8 @@ def ns_normalize(G, eps: float = DEFAULT_EPS, transpose_tall: bool = True,
 def ns_syrk(X):
     """R = X X^T for an fp16 (s, l) GPU matrix (s % 256 == 0, l % 64 == 0)."""
     torch = _torch()
+    if X.dim() != 2 or X.dtype != torch.float16:
+        raise ValueError("X must be a 2-D fp16 tensor")
     _device_tensor(X, "X")
     X = X.contiguous()
     s, l = X.shape
@@ -455,11 +460,20 @@ def ns_gemm_nt(A, B, C=None, alpha: float = 1.0, beta: float = 0.0,
                gamma: float = 0.0, symmetric: bool = False):
     """alpha A B^T + beta C + gamma I on fp16 GPU matrices."""
     torch = _torch()
-    A, B = _device_tensor(A, "A").contiguous(), _device_tensor(B, "B").contiguous()
+    for name, t in (("A", A), ("B", B), ("C", C)):
+        if t is not None and (t.dim() != 2 or t.dtype != torch.float16):
+            raise ValueError(f"{name} must be a 2-D fp16 tensor")
     M, K = A.shape
     N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError(f"B has {B.shape[1]} columns, A has {K}")
+    if C is not None and tuple(C.shape) != (M, N):
+        raise ValueError(f"C has shape {tuple(C.shape)}, expected {(M, N)}")
+    A, B = _device_tensor(A, "A").contiguous(), _device_tensor(B, "B").contiguous()
+    if C is not None:
+        C = _device_tensor(C, "C").contiguous()
     D = torch.empty((M, N), dtype=torch.float16, device=A.device)
-    cptr = C.contiguous().data_ptr() if C is not None else None
+    cptr = C.data_ptr() if C is not None else None
     ws = _workspace(NS_UNIT_WORKSPACE_BYTES, A.device)
     _check(library().ns_gemm_nt(A.data_ptr(), B.data_ptr(), cptr, D.data_ptr(), M, N, K,
                                 alpha, beta, gamma, 1 if symmetric else 0, ws.data_ptr(),

@@ -327,3 +327,20 @@ def test_output_overlapping_its_input_is_refused():
     m = nsmi._Matrix(base, nsmi.NS_DT_F16, 8, 16, 16, base + 8 * 16 * 2, nsmi.NS_DT_F16, 16)
     assert lib.ns_batched(ctypes.byref(m), 1, nsmi.NS_GRAM, ctypes.byref(p), ctypes.c_void_p(1),
                           1 << 30, None) in (nsmi.NS_ERR_UNSUPPORTED, nsmi.NS_OK)
+
+
+def test_binding_checks_shapes_and_types_before_device_work():
+    """Shapes and dtypes the library would misread (reading past B, writing
+    past a small output) are refused in the binding, on CPU tensors too."""
+    import torch
+    with pytest.raises(ValueError, match="output shape"):
+        nsmi._matrix(torch.zeros(8, 16), torch.zeros(8, 8, dtype=torch.float16))
+    h = lambda *s: torch.zeros(*s, dtype=torch.float16)
+    with pytest.raises(ValueError, match="columns"):
+        nsmi.ns_gemm_nt(h(256, 128), h(256, 64))
+    with pytest.raises(ValueError, match="C has shape"):
+        nsmi.ns_gemm_nt(h(256, 128), h(256, 128), h(256, 128))
+    with pytest.raises(ValueError, match="fp16"):
+        nsmi.ns_gemm_nt(torch.zeros(256, 128), h(256, 128))
+    with pytest.raises(ValueError, match="fp16"):
+        nsmi.ns_syrk(torch.zeros(256, 128))
