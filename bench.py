@@ -167,12 +167,23 @@ def cpu_baseline(workload, restarts, budget_s):
     import workloads as W
     from oracle import COEFFICIENT_SETS, gram_newton_schulz
 
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 0) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [os.cpu_count()])
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 0) for i in libs] or [os.cpu_count()])
+        if libs:
+            blas = " ".join(str(libs[0].get(k, "")) for k in ("internal_api", "version",
+                                                              "architecture")).strip()
     except Exception:  # pragma: no cover - informational only
         threads = os.cpu_count()
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((line.split(":", 1)[1].strip() for line in f
+                              if line.startswith("model name")), cpu_model)
+    except OSError:  # pragma: no cover - informational only
+        pass
 
     w = W.WORKLOADS[workload]
     table = COEFFICIENT_SETS[w.coefficients]   # the oracle's own copy of the table
@@ -212,7 +223,8 @@ def cpu_baseline(workload, restarts, budget_s):
                  "; unmeasured classes scaled by fp64 flop count"))
     return {"value": len(w.shapes) / total, "unit": "matrices/s", "cores": int(threads),
             "kind": "oracle", "sample": sample, "batch_seconds_est": total,
-            "sample_seconds": spent, "cpu_count": os.cpu_count()}
+            "sample_seconds": spent, "cpu_count": os.cpu_count(), "cpu_model": cpu_model,
+            "blas": blas}
 
 
 def main():
