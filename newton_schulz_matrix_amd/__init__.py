@@ -499,7 +499,7 @@ class NewtonSchulz:
     """Configured NS operator (the page's NewtonSchulz(...) object).
 
     backend: "gram" or "direct" (the algorithm axis). kernel: "auto" or
-    "hip-mfma-f16"; this build has one kernel set, so any other explicit
+    "hip-mfma-f16"; this library has one kernel set, so any other explicit
     kernel name (the page's CUDA kernels among them) raises at construction,
     as the page specifies for an unavailable explicit kernel, and so does an
     explicit "hip-mfma-f16" when no gfx950 device is visible. deterministic:
@@ -513,7 +513,7 @@ class NewtonSchulz:
         if backend not in ("gram", "direct"):
             raise ValueError(f"unknown backend {backend!r} (expected 'gram' or 'direct')")
         if kernel not in KERNELS:
-            raise ValueError(f"kernel {kernel!r} is not available in this build "
+            raise ValueError(f"kernel {kernel!r} is not available in this library "
                              f"(available: {', '.join(KERNELS)})")
         library()   # fails loudly when the library has not been built
         if kernel != "auto" and not get_backend_status()["gfx950_available"]:
