@@ -85,6 +85,29 @@ def test_owner_batch_bench_configuration(backend):
         assert err <= BAR
 
 
+def test_owner_batch_output_dtypes():
+    """The owner batch in the benchmark's launch configuration with fp32 and
+    bf16 outputs: every output type is one rounding of the same fp32
+    accumulator, so each must match the fp16 output to within the coarser of
+    the two roundings (relative Frobenius 2^-10 for fp32 vs fp16, 2^-8 for
+    bf16), and fp32 must lie closer to the oracle-checked fp16 result than
+    bf16 does on average."""
+    require_gpu()
+    Gs, o16 = _gpu_batched(4)
+    _, o32 = _gpu_batched(4, out_dtype=torch.float32)
+    _, obf = _gpu_batched(4, out_dtype=torch.bfloat16)
+    e32, ebf = [], []
+    for a, b, c in zip(o16, o32, obf):
+        assert b.dtype == torch.float32 and c.dtype == torch.bfloat16
+        A = to64(a)
+        e32.append(rel_fro(to64(b), A))
+        ebf.append(rel_fro(to64(c), A))
+    print(f"fp32 vs fp16 max {max(e32):.2e}, bf16 vs fp16 max {max(ebf):.2e}", flush=True)
+    assert max(e32) <= 2.0 ** -10
+    assert max(ebf) <= 2.0 ** -8
+    assert np.mean(e32) < np.mean(ebf)
+
+
 @pytest.mark.parametrize("j", range(8))
 def test_controlled_spectrum(j):
     require_gpu()
