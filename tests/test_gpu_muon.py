@@ -113,3 +113,35 @@ def test_muon_three_steps():
     err = rel_fro(to64(p) - to64(P), P64 - to64(P))
     print(f"three steps: accumulated update rel err {err:.3e}", flush=True)
     assert err <= 1e-2
+
+
+def test_muon_step_owner_batch_full_size():
+    """The fused Muon step on the 28-matrix owner batch in the benchmark's
+    configuration (bf16 gradients, fp32 momentum and parameters, Polar
+    Express, restart [2], beta 0.95, lr 0.02): one matrix of each Gram shape
+    class against the oracle (momentum within one fp32 ulp, update at the
+    1e-2 bar). Momentum and parameters are drawn on the device from a seeded
+    generator."""
+    require_gpu()
+    from oracle import COEFFICIENT_SETS
+    w = W.WORKLOADS[4]
+    Gs = [W.matrix(4, j).cuda() for j in range(len(w.shapes))]
+    gen = torch.Generator(device="cuda").manual_seed(404)
+    Ms = [torch.randn(G.shape, generator=gen, device="cuda") for G in Gs]
+    Ps = [torch.randn(G.shape, generator=gen, device="cuda") * 0.02 for G in Gs]
+    M0 = {j: Ms[j].cpu() for j in (0, 1, 4)}          # q 4096^2, k 1024x4096, gate 14336x4096
+    P0 = {j: Ps[j].cpu() for j in (0, 1, 4)}
+    beta, lr = 0.95, 0.02
+    nsmi.ns_muon_step(Gs, Ms, Ps, beta, lr, None, nsmi.COEFFICIENT_SETS[w.coefficients],
+                      w.restarts)
+    torch.cuda.synchronize()
+    for j in (0, 1, 4):
+        M1, P1 = muon_step(to64(Gs[j].cpu()), to64(M0[j]), to64(P0[j]),
+                           np.float64(np.float32(beta)), lr, 1.0,
+                           COEFFICIENT_SETS[w.coefficients], w.restarts)
+        u = _ulps32(Ms[j].cpu().numpy(), M1)
+        assert u.max() <= 1
+        upd = (to64(Ps[j]) - to64(P0[j])) / (-np.float64(np.float32(lr)))
+        err = rel_fro(upd, (P1 - to64(P0[j])) / (-lr))
+        print(f"muon owner batch #{j} {tuple(Gs[j].shape)}: update rel err {err:.3e}", flush=True)
+        assert err <= 1e-2
