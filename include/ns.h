@@ -34,7 +34,10 @@
  *               inputs or the workspace; a matrix whose output range
  *               overlaps its own input range is refused (NS_ERR_INVALID_ARG),
  *               other overlaps are the caller's to avoid. Concurrent calls on
- *               different streams need different workspaces.
+ *               different streams need different workspaces. Calls are not
+ *               meant for HIP graph capture: each one copies its launch
+ *               descriptors from a pinned host staging slot that later calls
+ *               reuse, so a captured copy would replay stale descriptors.
  *   Errors      Return codes only: nothing is printed and nothing is thrown.
  *               Argument checks run on the host before any device work; on
  *               any error other than NS_ERR_HIP nothing has been enqueued.
