@@ -97,6 +97,25 @@ def gemm_traffic_per_launch():
     return float(m.group(1))
 
 
+def pages_flops(shapes, steps, restarts):
+    """Gram flops per call in the pages' own count: the SYRKs R = X X^T at
+    s (s + 1) l (the half-tile saving the pages describe), the restart and
+    output products Q X at 2 s^2 l, and every s^3 product of the iteration at
+    2 s^3 (no symmetric saving). With r effective restarts the iteration has
+    K Z products, K - 1 - r Q updates (the first after a start or restart is
+    Q = Z + a I) and two products per R recurrence (k + 1 < K, k + 1 not a
+    restart)."""
+    K = steps
+    S = {int(i) for i in restarts if 0 < int(i) < K}
+    r = len(S)
+    m3 = K + (K - 1 - r) + 2 * sum(1 for k in range(K - 1) if (k + 1) not in S)
+    total = 0.0
+    for (m, n) in shapes:
+        s_, l_ = min(m, n), max(m, n)
+        total += (1 + r) * s_ * (s_ + 1) * l_ + (1 + r) * 2.0 * s_ * s_ * l_ + m3 * 2.0 * s_ ** 3
+    return total
+
+
 def time_backend(nsmi, torch, Gs, outs, backend, table, restarts, steps, warmup):
     """Warm up, then time exactly `steps` grouped calls; returns a dict."""
     ws = torch.empty(nsmi.ns_workspace_size([tuple(G.shape) for G in Gs], backend, table,
@@ -227,6 +246,19 @@ def cpu_baseline(workload, restarts, budget_s):
             "blas": blas}
 
 
+def target_line(n, w, ms, steps):
+    """The throughput at which the pages' flop count for the batch (see
+    pages_flops) takes 50% of the fp16 dense peak, and value against it.
+    Informational: matrices/s is implementation-neutral; the TFLOP/s and
+    roofline figures elsewhere count only the work this path does."""
+    f = pages_flops(w.shapes, steps, w.restarts)
+    t = n / (f / (0.5 * PEAK_FP16_TFLOPS * 1e12))
+    return {"matrices_per_s": t, "value_over_target": (n / (ms * 1e-3)) / t,
+            "pages_flops_per_step": f,
+            "basis": "50% of the fp16 dense peak for the pages' flop count of the batch "
+                     "(SYRK at s(s+1)l, Q X at 2s^2 l, every s^3 product at 2s^3)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -309,6 +341,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
+        "target": target_line(n, w, ms, len(table)),
         "config": {"workload": f"Llama-3-8B owner share: 28 projections (4 x q/k/v/o/gate/up/"
                                f"down), bf16 N(0,1) gradients, one ns_batched call",
                    "matrices": n, "backend": args.backend, "coefficients": w.coefficients,

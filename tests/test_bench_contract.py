@@ -58,3 +58,20 @@ def test_cpu_baseline_keys():
     assert out["kind"] == "oracle" and out["unit"] == "matrices/s"
     assert out["value"] > 0 and out["cores"] >= 1
     json.dumps(out)
+
+
+def test_pages_flop_count():
+    """The pages' Gram flop count per call (SYRK at s(s+1)l, Q X at 2s^2 l,
+    s^3 products at 2s^3; 14 of them for restarts [2], 11 for [1, 3]) on
+    three workloads, against the closed form evaluated by hand."""
+    def closed(s, l, r, m3):
+        return (1 + r) * s * (s + 1) * l + (1 + r) * 2 * s * s * l + m3 * 2 * s ** 3
+    assert bench.pages_flops([(256, 1024)], 5, (2,)) == closed(256, 1024, 1, 14)
+    assert bench.pages_flops([(8192, 2048)], 5, (1, 3)) == closed(2048, 8192, 2, 11)
+    llama = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096),
+             (14336, 4096), (14336, 4096), (4096, 14336)] * 4
+    want = sum(closed(min(s), max(s), 1, 14) for s in llama)
+    assert bench.pages_flops(llama, 5, (2,)) == want
+    assert abs(want / 1e12 - 59.547) < 1e-3
+    # restart 0 and out-of-range indices are no restarts
+    assert bench.pages_flops([(64, 64)], 5, (0,)) == closed(64, 64, 0, 5 + 4 + 8)
