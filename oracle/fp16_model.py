@@ -13,6 +13,13 @@ evaluated in fp32 before that rounding.
 ``symmetric=True`` models an implementation that computes only the lower
 triangle of each Gram-space product (all of them are symmetric in exact
 arithmetic) and mirrors it.
+
+``literal=True`` (Gram space only) models the plainest library rendering of
+the page's equations instead: every product is a full matrix product in the
+shape of a general multiply or multiply-add (Z = b R + c R R, Q <- a Q + Z Q),
+nothing is mirrored, and R is evolved in the form the recurrence follows
+from, R <- (a I + Z) R (a I + Z), with the factor (a I + Z) stored in fp16 and
+each of the two products rounded to fp16.
 """
 
 from __future__ import annotations
@@ -53,7 +60,12 @@ def direct_fp16(G, coefficients, eps: float = 1e-7, symmetric: bool = False,
 
 
 def gram_fp16(G, coefficients, restart_iterations=(2,), eps: float = 1e-7,
-              symmetric: bool = False, out_fp32: bool = False) -> np.ndarray:
+              symmetric: bool = False, out_fp32: bool = False,
+              literal: bool = False) -> np.ndarray:
+    if literal:
+        if symmetric:
+            raise ValueError("the literal-order model mirrors nothing")
+        return _gram_fp16_literal(G, coefficients, restart_iterations, eps, out_fp32)
     X, _ = normalize_fp16(G, eps)
     tall = X.shape[0] > X.shape[1]
     if tall:
@@ -79,6 +91,34 @@ def gram_fp16(G, coefficients, restart_iterations=(2,), eps: float = 1e-7,
         if k + 1 < K and (k + 1) not in S:
             T = _h(f(Z @ R + a * R))
             R = _h(f(T @ Z + a * T))
+    out = Q @ X
+    if not out_fp32:
+        out = _h(out)
+    return out.T.copy() if tall else out
+
+
+def _gram_fp16_literal(G, coefficients, restart_iterations, eps, out_fp32):
+    """Gram-space iteration in the order the page writes it (see module doc)."""
+    X, _ = normalize_fp16(G, eps)
+    tall = X.shape[0] > X.shape[1]
+    if tall:
+        X = X.T.copy()
+    K = len(coefficients)
+    S = set(int(i) for i in restart_iterations)
+    eye = np.eye(X.shape[0], dtype=np.float32)
+    R = _h(X @ X.T)
+    Q = None
+    for k, (a, b, c) in enumerate(coefficients):
+        a, b, c = np.float32(a), np.float32(b), np.float32(c)
+        if k in S and Q is not None:
+            X = _h(Q @ X)
+            R = _h(X @ X.T)
+            Q = None
+        Z = _h(b * R + c * (R @ R))
+        Q = _h(Z + a * eye) if Q is None else _h(a * Q + Z @ Q)
+        if k + 1 < K and (k + 1) not in S:
+            M = _h(a * eye + Z)
+            R = _h(_h(M @ R) @ M)
     out = Q @ X
     if not out_fp32:
         out = _h(out)

@@ -47,12 +47,18 @@ def run_oracle(G, backend, table, restarts=(2,)):
     return direct_newton_schulz(G64, co)
 
 
-def model_floor(G, backend, table, restarts=(2,)):
+def model_floor(G, backend, table, restarts=(2,), literal=False):
+    """Error of an fp16 rounding model of the method against the oracle.
+    literal=False: the model mirrors symmetric products as the library does;
+    literal=True (gram only): full products in the page's multiply-add
+    shape, R evolved as (a I + Z) R (a I + Z), nothing mirrored, i.e. a model
+    that shares none of the library's ordering choices."""
     co = TABLES[table][0]
     G64 = to64(G)
     ref = run_oracle(G, backend, table, restarts)
     if backend == "gram":
-        emu = fp16_model.gram_fp16(G64, co, restarts, symmetric=True)
+        emu = (fp16_model.gram_fp16(G64, co, restarts, literal=True) if literal
+               else fp16_model.gram_fp16(G64, co, restarts, symmetric=True))
     else:
         emu = fp16_model.direct_fp16(G64, co, symmetric=True)
     return rel_fro(emu, ref)
@@ -75,12 +81,18 @@ def test_cfg1_gram_within_fp16_floor():
     out = run_gpu(G, "gram", "pe")
     err = rel_fro(to64(out), run_oracle(G, "gram", "pe"))
     floor = model_floor(G, "gram", "pe")
-    print(f"256x1024 gram PE: rel err {err:.3e}, fp16 model floor {floor:.3e}", flush=True)
+    literal = model_floor(G, "gram", "pe", literal=True)
+    print(f"256x1024 gram PE: rel err {err:.3e}, fp16 model floor {floor:.3e} (mirrored), "
+          f"{literal:.3e} (literal order)", flush=True)
+    # both bars: the model built like the library, and one that shares none
+    # of its ordering choices (1.15e-2 and 1.20e-2 on this input)
     assert err <= 1.5 * floor
+    assert err <= 1.5 * literal
 
 
 @pytest.mark.xfail(reason="fp16 rounding floor of the method with the printed Polar Express "
-                          "table on this input is ~1.15e-2 (fp16 model), above 1e-2",
+                          "table on this input is 1.15e-2 (mirrored fp16 model) and 1.20e-2 "
+                          "(literal-order fp16 model), above 1e-2; the GPU measured 1.19e-2",
                    strict=False)
 def test_cfg1_gram_one_percent():
     require_gpu()
