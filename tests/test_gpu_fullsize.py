@@ -14,6 +14,11 @@
   output spectrum, and on two matrices also u_i^T out v_i with p(sigma_hat_i)
   per index.
 * Largest accepted side (65536) and ragged full-size shapes.
+
+Every full-size comparison also checks each 256 x 256 tile of the output:
+no tile's relative error may exceed twice the whole matrix's (the fp16
+rounding model's worst tile is within 1.06x on these inputs), so one wrong
+tile cannot hide inside a whole-matrix norm.
 """
 
 import numpy as np
@@ -22,7 +27,7 @@ import torch
 
 import newton_schulz_matrix_amd as nsmi
 import workloads as W
-from gpu_helpers import rel_fro, require_gpu, to64
+from gpu_helpers import assert_tiles_uniform, rel_fro, require_gpu, to64
 from oracle import COEFFICIENT_SETS, direct_newton_schulz, gram_newton_schulz, scalar_map
 
 pytestmark = pytest.mark.gpu
@@ -51,8 +56,8 @@ def test_kv_batch_16x1024x4096():
     require_gpu()
     Gs, outs = _gpu_batched(2)
     for j, (G, o) in enumerate(zip(Gs, outs)):
-        err = rel_fro(to64(o), _oracle(G.cpu(), 2))
-        print(f"1024x4096 #{j}: rel err {err:.3e}", flush=True)
+        err, worst = assert_tiles_uniform(to64(o), _oracle(G.cpu(), 2), what=f"1024x4096 #{j}")
+        print(f"1024x4096 #{j}: rel err {err:.3e} (worst tile {worst:.3e})", flush=True)
         assert err <= BAR
 
 
@@ -60,8 +65,9 @@ def test_llama_layer():
     require_gpu()
     Gs, outs = _gpu_batched(3)
     for name, G, o in zip(W.WORKLOADS[3].labels, Gs, outs):
-        err = rel_fro(to64(o), _oracle(G.cpu(), 3))
-        print(f"layer {name} {tuple(G.shape)}: rel err {err:.3e}", flush=True)
+        err, worst = assert_tiles_uniform(to64(o), _oracle(G.cpu(), 3), what=name)
+        print(f"layer {name} {tuple(G.shape)}: rel err {err:.3e} (worst tile {worst:.3e})",
+              flush=True)
         assert err <= BAR
 
 
@@ -77,11 +83,15 @@ def test_owner_batch_bench_configuration(backend):
                   else nsmi.ns_direct(G, table))
         torch.cuda.synchronize()
         assert torch.equal(o, single)
-    # one matrix of each Gram shape class vs the oracle
-    samples = {"gram": [1, 7, 27], "direct": [2, 14]}[backend]
+    # vs the oracle, on the batch's own inputs: one matrix of each shape
+    # orientation class (k/v 1024x4096, q/o 4096^2, tall gate/up 14336x4096,
+    # wide down 4096x14336), for both backends
+    samples = {"gram": [1, 4, 7, 27], "direct": [2, 4, 6, 14]}[backend]
     for j in samples:
-        err = rel_fro(to64(outs[j]), _oracle(Gs[j].cpu(), 4, backend))
-        print(f"{backend} {w.labels[j]} {tuple(Gs[j].shape)}: rel err {err:.3e}", flush=True)
+        err, worst = assert_tiles_uniform(to64(outs[j]), _oracle(Gs[j].cpu(), 4, backend),
+                                          what=f"{backend} {w.labels[j]}")
+        print(f"{backend} {w.labels[j]} {tuple(Gs[j].shape)}: rel err {err:.3e} "
+              f"(worst tile {worst:.3e})", flush=True)
         assert err <= BAR
 
 
@@ -119,7 +129,8 @@ def test_controlled_spectrum(j):
     torch.cuda.synchronize()
     got = to64(out)
     G64 = to64(G)
-    err = rel_fro(got, gram_newton_schulz(G64, co, w.restarts))
+    err, _ = assert_tiles_uniform(got, gram_newton_schulz(G64, co, w.restarts),
+                                  what=f"spectrum #{j}")
     nu = np.linalg.norm(G64)
     want_vectors = j < 2
     if want_vectors:
@@ -150,6 +161,6 @@ def test_max_side_and_ragged(shape):
         oco = COEFFICIENT_SETS["you"]
         ref = (gram_newton_schulz(to64(G), oco, (2,)) if backend == "gram"
                else direct_newton_schulz(to64(G), oco))
-        err = rel_fro(to64(out), ref)
-        print(f"{backend} {shape}: rel err {err:.3e}", flush=True)
+        err, worst = assert_tiles_uniform(to64(out), ref, what=f"{backend} {shape}")
+        print(f"{backend} {shape}: rel err {err:.3e} (worst tile {worst:.3e})", flush=True)
         assert err <= BAR
