@@ -34,13 +34,24 @@
  *               inputs or the workspace; a matrix whose output range
  *               overlaps its own input range is refused (NS_ERR_INVALID_ARG),
  *               other overlaps are the caller's to avoid. Concurrent calls on
- *               different streams need different workspaces. Calls are not
- *               meant for HIP graph capture: each one copies its launch
- *               descriptors from a pinned host staging slot that later calls
- *               reuse, so a captured copy would replay stale descriptors.
+ *               different streams need different workspaces.
+ *   Workspace   Device memory of the size the matching *_workspace_size
+ *               function reports, 256-byte aligned (NS_ERR_WORKSPACE
+ *               otherwise), with no required contents: every call writes
+ *               what it reads. The call also writes its launch descriptors
+ *               there.
+ *   Graphs      A call enqueues kernel launches only (its descriptor tables
+ *               travel as kernel arguments of small fill launches; there are
+ *               no host-to-device copies, memsets or host waits), so it can
+ *               be captured into a HIP graph and replayed, provided the
+ *               captured buffers stay allocated and timing is disabled.
  *   Errors      Return codes only: nothing is printed and nothing is thrown.
  *               Argument checks run on the host before any device work; on
  *               any error other than NS_ERR_HIP nothing has been enqueued.
+ *               Before launching, every byte range the planned kernels can
+ *               read or write is checked on the host against the workspace
+ *               buffers and the caller's matrices (NS_ERR_INTERNAL if one
+ *               falls outside; ns_plan_check exposes the same check).
  *               NaN or Inf in the input propagate to the output.
  *   Device      The current HIP device must be a gfx950 GPU, otherwise
  *               NS_ERR_UNSUPPORTED.
@@ -65,7 +76,10 @@ typedef enum {
   NS_ERR_INVALID_ARG = 1,  /* a size, pointer, dtype or parameter is invalid */
   NS_ERR_UNSUPPORTED = 2,  /* no HIP device, or the device is not gfx950    */
   NS_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required   */
-  NS_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed    */
+  NS_ERR_HIP = 4,          /* a HIP runtime call or kernel launch failed    */
+  NS_ERR_INTERNAL = 5      /* the launch plan failed the library's own
+                              bounds check (a library defect); nothing was
+                              enqueued                                       */
 } ns_status;
 
 typedef enum { NS_DT_F32 = 0, NS_DT_BF16 = 1, NS_DT_F16 = 2 } ns_dtype;
@@ -250,6 +264,81 @@ ns_status ns_gemm_nt(const void* a, const void* b, const void* c, void* d,
                      int64_t M, int64_t N, int64_t K, float alpha, float beta,
                      float gamma, int symmetric, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* One product of the grouped GEMM kernel with every option the iteration's
+ * stages use, exposed for kernel-level testing of that path (the building
+ * blocks above use only row-major operands and none of the second outputs).
+ * The kernel computes, for i < M, j < N (fp32, rounded once per output):
+ *   v = alpha * sum_k A[i][k] B[j][k] + beta * C[i][j] + (i == j < diag_n ? gamma : 0)
+ *   d[i][j]  = v                                (type d_dtype, leading dim ldd)
+ *   d2[i][j] = v + (i == j < diag_n ? delta : 0)           (fp16, leading dim N)
+ *   dt[j][i] = v                                 (fp16, leading dim M)
+ *   a (M, K) and b (N, K): fp16, leading dimension K;
+ *   c (M, N): type c_dtype, leading dimension ldc, or NULL (then beta is
+ *             not used);
+ *   *_pairs:  1 = the row-pair layout the iteration keeps its fp16 buffers
+ *             in (rows even, leading dimension a multiple of 32): element
+ *             (i, j) at (i / 2) * 2 ld + (j / 32) * 64 + (i % 2) * 32 + j % 32;
+ *             0 = row-major. d_pairs applies to d, d2 and dt;
+ *   symmetric: M == N, only tiles on or below the diagonal are computed and
+ *             each is also stored mirrored, so d (and d2) come out exactly
+ *             symmetric; requires fp16 c and d, no dt;
+ *   c_is_bt:  the caller guarantees c[i][j] == b[j][i] (needs M <= K,
+ *             alpha != 0); beta * c is then taken from the B slices the
+ *             product already streams instead of being read again;
+ *   valid_m, valid_n: stores (and reads of c) are clipped to this block when
+ *             the output is not an fp16 tile-aligned buffer; d2 and dt
+ *             need the unclipped fp16 path (valid block == M x N, fp16 d,
+ *             16-byte aligned, ldd % 8 == 0) or the symmetric mode.
+ * M, N multiples of 256, K a multiple of 128, all sides <= NS_MAX_DIM.
+ * Problems share one launch, ordered as the iteration's stages order them
+ * (longer K first); the workspace holds the launch descriptors
+ * (ns_gemm_grouped_workspace_size). Asynchronous on `stream`; errors as
+ * for every entry point. */
+typedef struct {
+  const void* a;
+  const void* b;
+  const void* c;
+  void* d;
+  void* d2;
+  void* dt;
+  int64_t M, N, K, ldc, ldd;
+  int64_t valid_m, valid_n, diag_n;
+  ns_dtype c_dtype, d_dtype;
+  int symmetric, c_is_bt;
+  int a_pairs, b_pairs, c_pairs, d_pairs;
+  float alpha, beta, gamma, delta;
+} ns_gemm_problem;
+ns_status ns_gemm_grouped_workspace_size(int count, size_t* bytes);
+ns_status ns_gemm_grouped(const ns_gemm_problem* probs, int count, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* Host-side self-check of a call's launch plan (testing and diagnostics;
+ * needs no device, launches nothing and dereferences no pointer). Builds the
+ * plan that ns_batched (entry NS_CHECK_BATCHED; mats is an ns_matrix array),
+ * ns_gram_sharded (NS_CHECK_SHARDED; one ns_matrix, `shards` shards) or
+ * ns_muon_step (NS_CHECK_MUON; mats is an ns_muon_matrix array) would
+ * launch for these arguments with its workspace at address `ws`, and runs
+ * the bounds check every call runs before launching: each byte range a
+ * kernel of the plan can read or write, derived from its descriptors the
+ * way the kernels address memory, must lie inside one workspace buffer of
+ * the plan's layout or one caller matrix, with write permission where it is
+ * written. ws_bytes == 0 takes the required size. `plant` != 0 first plants
+ * one of these mistakes into the plan, so a test can see the check catch it
+ * (NS_ERR_UNSUPPORTED if the plan has no place for it):
+ *   1 a caller's C read over the whole padded tile instead of its real block
+ *   2 a caller's output written over the whole padded tile
+ *   3 a product reading one K block past its operands
+ *   4 the cast writing 64 rows past its padded block
+ *   5 the norm pass reading one row past the input
+ *   6 a shard reduction running one block past its parts
+ * Returns NS_OK, NS_ERR_INTERNAL (first violation described in msg, if msg
+ * is not NULL, truncated to msg_len bytes), or the status the entry point's
+ * argument checks give. */
+typedef enum { NS_CHECK_BATCHED = 0, NS_CHECK_SHARDED = 1, NS_CHECK_MUON = 2 } ns_check_entry;
+ns_status ns_plan_check(ns_check_entry entry, const void* mats, int count, ns_backend backend,
+                        int shards, const ns_params* params, void* ws, size_t ws_bytes,
+                        int plant, char* msg, size_t msg_len);
 
 /* Kernel timing (measurement aid). While enabled, every launch made by
  * ns_normalize / ns_gram / ns_gram_sharded / ns_direct / ns_batched /

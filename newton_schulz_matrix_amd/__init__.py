@@ -44,7 +44,9 @@ COEFFICIENT_SETS = {"polar_express": POLAR_EXPRESS_COEFFICIENTS,
 DEFAULT_RESTARTS = (2,)
 DEFAULT_EPS = 1e-7
 
-NS_OK, NS_ERR_INVALID_ARG, NS_ERR_UNSUPPORTED, NS_ERR_WORKSPACE, NS_ERR_HIP = range(5)
+(NS_OK, NS_ERR_INVALID_ARG, NS_ERR_UNSUPPORTED, NS_ERR_WORKSPACE, NS_ERR_HIP,
+ NS_ERR_INTERNAL) = range(6)
+NS_CHECK_BATCHED, NS_CHECK_SHARDED, NS_CHECK_MUON = range(3)
 NS_DT_F32, NS_DT_BF16, NS_DT_F16 = 0, 1, 2
 NS_GRAM, NS_DIRECT = 0, 1
 NS_UNIT_WORKSPACE_BYTES = 4096
@@ -91,6 +93,21 @@ class _MuonMatrix(ctypes.Structure):
                 ("ld_param", ctypes.c_int64), ("scale", ctypes.c_float)]
 
 
+class _GemmProblem(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("c", ctypes.c_void_p),
+                ("d", ctypes.c_void_p), ("d2", ctypes.c_void_p), ("dt", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("ldc", ctypes.c_int64), ("ldd", ctypes.c_int64),
+                ("valid_m", ctypes.c_int64), ("valid_n", ctypes.c_int64),
+                ("diag_n", ctypes.c_int64),
+                ("c_dtype", ctypes.c_int), ("d_dtype", ctypes.c_int),
+                ("symmetric", ctypes.c_int), ("c_is_bt", ctypes.c_int),
+                ("a_pairs", ctypes.c_int), ("b_pairs", ctypes.c_int),
+                ("c_pairs", ctypes.c_int), ("d_pairs", ctypes.c_int),
+                ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
+                ("gamma", ctypes.c_float), ("delta", ctypes.c_float)]
+
+
 class _Matrix(ctypes.Structure):
     _fields_ = [("g", ctypes.c_void_p),
                 ("g_dtype", ctypes.c_int),
@@ -131,6 +148,10 @@ def library() -> ctypes.CDLL:
             "ns_syrk": [vp, i64, i64, vp, vp, sz, vp],
             "ns_gemm_nt": [vp, vp, vp, vp, i64, i64, i64, ctypes.c_float, ctypes.c_float,
                            ctypes.c_float, ctypes.c_int, vp, sz, vp],
+            "ns_gemm_grouped_workspace_size": [ctypes.c_int, ctypes.POINTER(sz)],
+            "ns_gemm_grouped": [ctypes.POINTER(_GemmProblem), ctypes.c_int, vp, sz, vp],
+            "ns_plan_check": [ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, P,
+                              vp, sz, ctypes.c_int, ctypes.c_char_p, sz],
         }
         for name, args in sigs.items():
             f = getattr(lib, name)
@@ -479,6 +500,68 @@ def ns_gemm_nt(A, B, C=None, alpha: float = 1.0, beta: float = 0.0,
                                 alpha, beta, gamma, 1 if symmetric else 0, ws.data_ptr(),
                                 ws.numel(), _stream_ptr(A)), "ns_gemm_nt")
     return D
+
+
+def ns_gemm_grouped(problems: List[dict]) -> None:
+    """Products of the grouped GEMM kernel with every descriptor option, in
+    one launch (kernel-level testing; see ns_gemm_problem in ns.h).
+
+    Each problem is a dict: "a", "b", "d" (GPU tensors; a and b fp16 holding
+    M*K and N*K elements in the layout their *_pairs flag names), optional
+    "c", "d2", "dt", the sizes "M", "N", "K", and optionally "ldc", "ldd"
+    (default N), "valid_m", "valid_n" (default M, N), "diag_n" (default 0),
+    "symmetric", "c_is_bt", "a_pairs", "b_pairs", "c_pairs", "d_pairs"
+    (default 0), "alpha" (1), "beta", "gamma", "delta" (0)."""
+    if not problems:
+        return
+    arr = (_GemmProblem * len(problems))()
+    dev = problems[0]["a"].device
+    for i, q in enumerate(problems):
+        for key in ("a", "b", "c", "d", "d2", "dt"):
+            if q.get(key) is not None:
+                _device_tensor(q[key], key)
+        M, N = int(q["M"]), int(q["N"])
+        c = q.get("c")
+        arr[i] = _GemmProblem(
+            q["a"].data_ptr(), q["b"].data_ptr(), c.data_ptr() if c is not None else None,
+            q["d"].data_ptr(),
+            q["d2"].data_ptr() if q.get("d2") is not None else None,
+            q["dt"].data_ptr() if q.get("dt") is not None else None,
+            M, N, int(q["K"]), int(q.get("ldc", N)), int(q.get("ldd", N)),
+            int(q.get("valid_m", M)), int(q.get("valid_n", N)), int(q.get("diag_n", 0)),
+            _dtype_code(c.dtype) if c is not None else NS_DT_F16, _dtype_code(q["d"].dtype),
+            int(q.get("symmetric", 0)), int(q.get("c_is_bt", 0)),
+            int(q.get("a_pairs", 0)), int(q.get("b_pairs", 0)),
+            int(q.get("c_pairs", 0)), int(q.get("d_pairs", 0)),
+            float(q.get("alpha", 1.0)), float(q.get("beta", 0.0)),
+            float(q.get("gamma", 0.0)), float(q.get("delta", 0.0)))
+    lib = library()
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.ns_gemm_grouped_workspace_size(len(problems), ctypes.byref(nbytes)),
+           "ns_gemm_grouped_workspace_size")
+    ws = _workspace(nbytes.value, dev)
+    _check(lib.ns_gemm_grouped(arr, len(problems), ws.data_ptr(), ws.numel(),
+                               _stream_ptr(problems[0]["a"])), "ns_gemm_grouped")
+
+
+def ns_plan_check(entry: int, mats, backend: str = "gram", shards: int = 1,
+                  coefficients=POLAR_EXPRESS_COEFFICIENTS,
+                  restart_iterations: Iterable[int] = DEFAULT_RESTARTS,
+                  eps: float = DEFAULT_EPS, ws: int = 1 << 40, ws_bytes: int = 0,
+                  plant: int = 0):
+    """Host-side bounds check of a call's launch plan (no device needed).
+
+    mats: a list of _Matrix (NS_CHECK_BATCHED, NS_CHECK_SHARDED) or
+    _MuonMatrix (NS_CHECK_MUON) records whose pointers are plain addresses
+    (never dereferenced). Returns (status, message)."""
+    typ = _MuonMatrix if entry == NS_CHECK_MUON else _Matrix
+    arr = (typ * len(mats))(*mats)
+    p, keep = _params(coefficients, restart_iterations, eps)
+    msg = ctypes.create_string_buffer(512)
+    st = library().ns_plan_check(entry, ctypes.cast(arr, ctypes.c_void_p), len(mats),
+                                 BACKENDS[backend], int(shards), ctypes.byref(p), ws,
+                                 ws_bytes, int(plant), msg, 512)
+    return st, msg.value.decode()
 
 
 def newton_schulz(G, backend: str = "gram", coefficients=POLAR_EXPRESS_COEFFICIENTS,

@@ -296,7 +296,27 @@ __global__ __launch_bounds__(256) void reduce_kernel(const ReduceDesc* __restric
   *reinterpret_cast<uint4*>(d.out + i0) = w;
 }
 
+// Descriptor table upload: `bytes` (a multiple of 16, at most TABLE_CHUNK)
+// from the kernel argument to dst, 16 bytes per thread.
+__global__ __launch_bounds__(128) void table_fill_kernel(unsigned char* __restrict__ dst,
+                                                         TableChunk chunk, int bytes) {
+  const int i = threadIdx.x * 16;
+  if (i < bytes) {
+    uint4 w;
+    __builtin_memcpy(&w, chunk.bytes + i, 16);
+    *reinterpret_cast<uint4*>(dst + i) = w;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_table_fill(unsigned char* dst, const TableChunk& chunk, int bytes,
+                             hipStream_t stream) {
+  static_assert(TABLE_CHUNK == 128 * 16, "one 16-byte piece per thread");
+  if (bytes <= 0) return hipSuccess;
+  hipLaunchKernelGGL(table_fill_kernel, dim3(1), dim3(128), 0, stream, dst, chunk, bytes);
+  return hipGetLastError();
+}
 
 hipError_t launch_reduce(const ReduceDesc* descs, int count, int total_blocks,
                          hipStream_t stream) {

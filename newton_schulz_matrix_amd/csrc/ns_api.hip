@@ -62,56 +62,24 @@ ns_status check_device() {
 }
 
 // ---------------------------------------------------------------- upload
-// Descriptor tables are copied from a pinned host staging ring (so the copy
-// is truly asynchronous and the source stays valid until it runs). A slot
-// is reused only after the copy recorded on it has completed.
-
-struct Slot {
-  void* host = nullptr;
-  size_t cap = 0;
-  hipEvent_t ev = nullptr;
-  bool pending = false;
-};
-constexpr int RING = 8;
-struct Ring {
-  Slot slot[RING];
-  int next = 0;
-};
-std::mutex g_up_mu;
-std::map<int, Ring> g_rings;
+// Descriptor tables are copied into the workspace by fill-kernel launches
+// whose arguments carry the bytes (TABLE_CHUNK per launch). Nothing on the
+// host has to stay alive after the call returns, no host memory is
+// allocated, and a call made under HIP graph capture records only kernel
+// launches, so replaying the graph rewrites the same table.
 
 hipError_t upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(g_up_mu);
-  Ring& ring = g_rings[dev];
-  Slot& s = ring.slot[ring.next];
-  ring.next = (ring.next + 1) % RING;
-  if (s.pending) {
-    e = hipEventSynchronize(s.ev);
-    if (e != hipSuccess) return e;
-    s.pending = false;
-  }
-  if (!s.ev) {
-    e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
+  const unsigned char* from = static_cast<const unsigned char*>(src);
+  unsigned char* to = static_cast<unsigned char*>(dst);
+  TableChunk chunk;
+  for (size_t off = 0; off < bytes; off += TABLE_CHUNK) {
+    const size_t n = std::min<size_t>(TABLE_CHUNK, bytes - off);
+    const size_t n16 = (n + 15) / 16 * 16;   // the destination is padded to 256 bytes
+    std::memcpy(chunk.bytes, from + off, n);
+    std::memset(chunk.bytes + n, 0, n16 - n);
+    const hipError_t e = launch_table_fill(to + off, chunk, static_cast<int>(n16), stream);
     if (e != hipSuccess) return e;
   }
-  if (s.cap < bytes) {
-    if (s.host) (void)hipHostFree(s.host);
-    s.host = nullptr;
-    s.cap = 0;
-    const size_t cap = std::max<size_t>(align_up(bytes, 65536), 65536);
-    e = hipHostMalloc(&s.host, cap, hipHostMallocPortable);
-    if (e != hipSuccess) return e;
-    s.cap = cap;
-  }
-  std::memcpy(s.host, src, bytes);
-  e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(s.ev, stream);
-  if (e != hipSuccess) return e;
-  s.pending = true;
   return hipSuccess;
 }
 
@@ -207,6 +175,7 @@ struct MatBuf {   // per-matrix workspace offsets (bytes from ws base)
 };
 
 struct Plan {
+  ns_backend backend = NS_GRAM;
   // Muon step (optional): per matrix the gradient added into the momentum
   // in the norm pass, and the update fused into the final product.
   const ns_muon_matrix* muon = nullptr;
@@ -643,6 +612,7 @@ void direct_stages(Builder& B, const ns_matrix* mats, const ns_params& p) {
 ns_status build_plan(Plan& pl, const ns_matrix* mats, int count, ns_backend be,
                      const ns_params& p, unsigned char* ws, int shards = 1,
                      const ns_muon_matrix* muon = nullptr, float beta = 0.f, float lr = 0.f) {
+  pl.backend = be;
   pl.muon = muon;
   pl.beta = beta;
   pl.lr = lr;
@@ -652,6 +622,327 @@ ns_status build_plan(Plan& pl, const ns_matrix* mats, int count, ns_backend be,
   else direct_stages(B, mats, p);
   pl.total = align_up(pl.table_off + pl.table.size());
   return NS_OK;
+}
+
+// ------------------------------------------------------------ bounds check
+// Before any launch, every byte range the kernels of a plan can touch is
+// derived from the plan's descriptors the way the kernels address memory
+// (see the kernels' load, store and epilogue paths), and must lie inside
+// one workspace buffer of the layout or one caller buffer, with write
+// permission where it is written. Adjacent buffers are not merged, so an
+// overrun into a neighbouring buffer is caught as well. A failure is a
+// planner bug: the call returns NS_ERR_INTERNAL and enqueues nothing.
+
+struct Iv {
+  uintptr_t lo, hi;
+  bool writable;
+};
+
+struct Bounds {
+  std::vector<Iv> raw;
+  std::vector<Iv> rd, wr;   // disjoint after finish(): readable, writable
+  std::string err;
+
+  void allow(const void* p, uintptr_t bytes, bool writable) {
+    if (!p || bytes == 0) return;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    raw.push_back({a, a + bytes, writable});
+  }
+  static void merge(std::vector<Iv>& v) {
+    std::sort(v.begin(), v.end(), [](const Iv& x, const Iv& y) { return x.lo < y.lo; });
+    std::vector<Iv> out;
+    for (const Iv& x : v) {
+      if (!out.empty() && x.lo < out.back().hi) out.back().hi = std::max(out.back().hi, x.hi);
+      else out.push_back(x);
+    }
+    v.swap(out);
+  }
+  void finish() {
+    for (const Iv& x : raw) {
+      rd.push_back(x);
+      if (x.writable) wr.push_back(x);
+    }
+    merge(rd);
+    merge(wr);
+  }
+  static bool inside(const std::vector<Iv>& v, uintptr_t lo, uintptr_t hi) {
+    auto it = std::upper_bound(v.begin(), v.end(), lo,
+                               [](uintptr_t x, const Iv& y) { return x < y.lo; });
+    if (it == v.begin()) return false;
+    --it;
+    return lo >= it->lo && hi <= it->hi;
+  }
+  bool fail(const std::string& what) {
+    if (err.empty()) err = what;
+    return false;
+  }
+  // elements [lo, hi) of `es` bytes from base
+  bool range(const char* what, const void* base, int64_t lo, int64_t hi, size_t es, bool write) {
+    if (!err.empty()) return false;
+    if (hi <= lo) return true;
+    if (!base) return fail(std::string(what) + ": null pointer");
+    const uintptr_t a = reinterpret_cast<uintptr_t>(base) + static_cast<uintptr_t>(lo) * es;
+    const uintptr_t b = reinterpret_cast<uintptr_t>(base) + static_cast<uintptr_t>(hi) * es;
+    if (!inside(write ? wr : rd, a, b)) {
+      char buf[256];
+      std::snprintf(buf, sizeof(buf), "%s: %s of bytes [%#llx, %#llx) outside every %s buffer",
+                    what, write ? "write" : "read", static_cast<unsigned long long>(a),
+                    static_cast<unsigned long long>(b), write ? "writable" : "readable");
+      return fail(buf);
+    }
+    return true;
+  }
+  // the (rows, cols) block at the origin of a matrix with leading dimension
+  // ld, row-major or in the row-pair layout
+  bool block(const char* what, const void* base, int64_t rows, int64_t cols, int64_t ld,
+             bool pairs, size_t es, bool write) {
+    if (rows <= 0 || cols <= 0) return true;
+    if (pairs && ld % 32) return fail(std::string(what) + ": row-pair layout needs ld % 32 == 0");
+    // the last element addressed, as the kernels compute it (also when a
+    // block is wider than its leading dimension)
+    const int64_t hi = pairs ? pair_index(rows - 1, cols - 1, ld) + 1 : (rows - 1) * ld + cols;
+    if (!range(what, base, 0, hi, es, write)) return false;
+    // a block wider than its leading dimension wraps into the next rows:
+    // inside the buffer, but someone else's elements
+    if (cols > ld) return fail(std::string(what) + ": block wider than its leading dimension");
+    return true;
+  }
+};
+
+size_t out_elem(int type) { return type == OUT_F32 ? 4 : 2; }
+
+// Which epilogue the GEMM kernel takes for a descriptor (mirrors the
+// dispatch at the end of gemm_nt_kernel).
+enum EpiKind { EK_SYM, EK_FAST, EK_GENERAL };
+EpiKind epilogue_kind(const GemmDesc& d) {
+  if (d.symmetric) return EK_SYM;
+  const void* C = d.c_is_bt ? nullptr : d.C;
+  const bool row_store_ok = (d.ldd % 8 == 0) && (reinterpret_cast<uintptr_t>(d.D) % 16 == 0);
+  if (d.out_type == OUT_F16 && d.valid_m == d.M && d.valid_n == d.N && row_store_ok && !d.D2 &&
+      (!C || d.c_type == OUT_F16))
+    return EK_FAST;
+  return EK_GENERAL;
+}
+
+bool check_gemm(const GemmDesc& d, Bounds& B) {
+  const int T = gemm_tile();
+  if (d.M <= 0 || d.N <= 0 || d.K <= 0 || d.M % T || d.N % T || d.K % gemm_k_multiple())
+    return B.fail("gemm: M, N or K is not a multiple of the tile");
+  if (d.symmetric && d.M != d.N) return B.fail("gemm: symmetric product that is not square");
+  const int tm = d.M / T, tn = d.N / T;
+  if (d.symmetric ? (d.tiles_n != tm || d.tiles != tm * (tm + 1) / 2)
+                  : (d.tiles_n != tn || d.tiles != tm * tn))
+    return B.fail("gemm: tile count does not match M and N");
+  if (d.valid_m < 0 || d.valid_m > d.M || d.valid_n < 0 || d.valid_n > d.N ||
+      d.diag_n < 0 || d.diag_n > std::min(d.M, d.N))
+    return B.fail("gemm: valid block or diagonal outside the product");
+  if (d.c_is_bt && (!d.C || d.M > d.K || d.alpha == 0.f))
+    return B.fail("gemm: C folded from B needs C, M <= K and alpha != 0");
+  B.block("gemm A", d.A, d.M, d.K, d.K, d.a_pairs, 2, false);
+  B.block("gemm B", d.B, d.N, d.K, d.K, d.b_pairs, 2, false);
+  const void* C = d.c_is_bt ? nullptr : d.C;
+  switch (epilogue_kind(d)) {
+    case EK_SYM:
+      if (d.out_type != OUT_F16 || (C && d.c_type != OUT_F16))
+        return B.fail("gemm: the symmetric epilogue is fp16 only");
+      if (d.DT) return B.fail("gemm: DT is ignored by the symmetric epilogue");
+      if (C) B.block("gemm C (symmetric)", C, d.M, d.N, d.ldc, d.c_pairs, 2, false);
+      B.block("gemm D (symmetric, mirrored)", d.D, d.M, d.N, d.ldd, d.d_pairs, 2, true);
+      if (d.D2) B.block("gemm D2", d.D2, d.M, d.N, d.N, d.d_pairs, 2, true);
+      break;
+    case EK_FAST:
+      if (C) B.block("gemm C (tile)", C, d.M, d.N, d.ldc, d.c_pairs, 2, false);
+      B.block("gemm D (tile)", d.D, d.M, d.N, d.ldd, d.d_pairs, 2, true);
+      if (d.DT) B.block("gemm DT", d.DT, d.N, d.M, d.M, d.d_pairs, 2, true);
+      break;
+    case EK_GENERAL:
+      if (d.D2 || d.DT) return B.fail("gemm: D2 / DT are ignored by the general epilogue");
+      if (C) B.block("gemm C (clipped)", C, d.valid_m, d.valid_n, d.ldc, d.c_pairs,
+                     out_elem(d.c_type), false);
+      B.block("gemm D (clipped)", d.D, d.valid_m, d.valid_n, d.ldd, d.d_pairs,
+              out_elem(d.out_type), true);
+      break;
+  }
+  return B.err.empty();
+}
+
+// Checks every descriptor of the plan; `ws` is the workspace base the plan
+// was built for.
+bool validate_plan(const Plan& pl, const unsigned char* ws, Bounds& B) {
+  const size_t tbytes = (pl.table.size() + 15) / 16 * 16;
+  B.range("descriptor table", ws, static_cast<int64_t>(pl.table_off),
+          static_cast<int64_t>(pl.table_off + tbytes), 1, true);
+  for (const Stage& st : pl.stages) {
+    const unsigned char* t = pl.table.data() + st.off;
+    switch (st.kind) {
+      case Stage::GEMM: {
+        const GemmDesc* d = reinterpret_cast<const GemmDesc*>(t);
+        int next = 0;
+        for (int i = 0; i < st.count; ++i) {
+          if (d[i].tile_begin != next) return B.fail("gemm: tile ranges not contiguous");
+          next += d[i].tiles;
+          if (!check_gemm(d[i], B)) return false;
+        }
+        if (next != st.total) return B.fail("gemm: launch size differs from its tiles");
+        break;
+      }
+      case Stage::SUMSQ:
+      case Stage::FINALIZE:
+      case Stage::CAST: {
+        const NormDesc* d = reinterpret_cast<const NormDesc*>(t);
+        int next = 0;
+        for (int i = 0; i < st.count; ++i) {
+          const NormDesc& n = d[i];
+          const size_t ge = out_elem(n.g_type);
+          if (st.kind == Stage::SUMSQ) {
+            if (n.chunk_begin != next) return B.fail("sumsq: chunk ranges not contiguous");
+            next += n.chunks;
+            if (n.chunks_n != ceil_div(n.n, SQ_COLS) || n.chunks != ceil_div(n.m, SQ_ROWS) * n.chunks_n)
+              return B.fail("sumsq: chunk count does not cover the matrix");
+            B.block("sumsq G", n.G, n.m, n.n, n.ldg, false, ge, n.grad != nullptr);
+            if (n.grad) B.block("sumsq gradient", n.grad, n.m, n.n, n.ldgrad, false,
+                                out_elem(n.grad_type), false);
+            B.range("sumsq partials", n.partials, n.chunk_begin, n.chunk_begin + n.chunks, 4, true);
+          } else if (st.kind == Stage::FINALIZE) {
+            B.range("finalize partials", n.partials, n.chunk_begin, n.chunk_begin + n.chunks, 4,
+                    false);
+            B.range("finalize norm", n.norm_slot, 0, 1, 4, true);
+            if (n.norm_out) B.range("finalize norm copy", n.norm_out, 0, 1, 4, true);
+          } else {
+            if (n.tile_begin != next) return B.fail("cast: tile ranges not contiguous");
+            next += n.tiles;
+            if (n.tiles_n != ceil_div(n.pn, CAST_TILE) ||
+                n.tiles != ceil_div(n.pm, CAST_TILE) * n.tiles_n)
+              return B.fail("cast: tile count does not cover the padded block");
+            if (n.m > n.pm || n.n > n.pn) return B.fail("cast: padded block smaller than G");
+            B.block("cast G", n.G, n.m, n.n, n.ldg, false, ge, false);
+            B.range("cast norm", n.norm_slot, 0, 1, 4, false);
+            if (n.P) B.block("cast X", n.P, n.pm, n.pn, n.ldp, n.pairs, 2, true);
+            if (n.PT) B.block("cast X^T", n.PT, n.pn, n.pm, n.ldpt, n.pairs, 2, true);
+          }
+          if (!B.err.empty()) return false;
+        }
+        if (st.kind != Stage::FINALIZE && next != st.total)
+          return B.fail("normalisation: launch size differs from its work");
+        break;
+      }
+      case Stage::REDUCE: {
+        const ReduceDesc* d = reinterpret_cast<const ReduceDesc*>(t);
+        int next = 0;
+        for (int i = 0; i < st.count; ++i) {
+          const ReduceDesc& r = d[i];
+          if (r.block_begin != next || r.elems % 8 || r.count < 1 || r.count > MAX_SHARDS)
+            return B.fail("reduce: malformed descriptor");
+          next += r.blocks;
+          for (int k = 0; k < r.count; ++k) B.range("reduce part", r.parts[k], 0, r.elems, 2, false);
+          B.range("reduce sum", r.out, 0, r.elems, 2, true);
+          if (!B.err.empty()) return false;
+        }
+        if (next != st.total) return B.fail("reduce: launch size differs from its blocks");
+        break;
+      }
+    }
+    if (!B.err.empty()) return false;
+  }
+  return B.err.empty();
+}
+
+// The buffers a call may touch: each workspace buffer of the layout, and the
+// caller's matrices (inputs read; outputs written; for the Muon step the
+// momentum read and written, the gradient read, the parameter read and
+// written).
+void allow_buffers(Bounds& B, const Plan& pl, const unsigned char* ws, const ns_matrix* mats,
+                   int count) {
+  for (int i = 0; i < count; ++i) {
+    const MatBuf& b = pl.mats[i];
+    const size_t ss = sq_bytes(b.Sp, b.Sp);
+    for (const Shard& h : b.sh) {
+      const size_t xl = sq_bytes(b.Sp, h.Lp);
+      B.allow(ws + h.X, xl, true);
+      B.allow(ws + h.XT[0], xl, true);
+      B.allow(ws + h.XT[1], xl, true);
+      if (b.sh.size() > 1) B.allow(ws + h.Rp, ss, true);
+    }
+    if (pl.backend == NS_GRAM) {
+      for (size_t off : {b.R, b.Z, b.T, b.Q[0], b.Q[1]}) B.allow(ws + off, ss, true);
+    } else {
+      B.allow(ws + b.A, ss, true);
+      B.allow(ws + b.B, ss, true);
+    }
+    const ns_matrix& a = mats[i];
+    const bool muon = pl.muon != nullptr;
+    const size_t gi = elem_bytes(a.g_dtype), oi = elem_bytes(a.out_dtype);
+    B.allow(a.g, ((a.m - 1) * a.ldg + a.n) * gi, muon);
+    B.allow(a.out, ((a.m - 1) * a.ldo + a.n) * oi, true);
+    if (muon) {
+      const ns_muon_matrix& u = pl.muon[i];
+      B.allow(u.grad, ((u.m - 1) * u.ld_grad + u.n) * elem_bytes(u.grad_dtype), false);
+    }
+  }
+  B.allow(ws + pl.partials_off, static_cast<size_t>(pl.total_chunks) * sizeof(float), true);
+  B.allow(ws + pl.norms_off, static_cast<size_t>(count) * sizeof(float), true);
+  B.allow(ws + pl.table_off, (pl.table.size() + 15) / 16 * 16, true);
+  B.finish();
+}
+
+// Deliberate mistakes planted into a built plan (test hook of ns_plan_check;
+// never applied on the launch path). Returns false if the plan has no
+// descriptor the mistake applies to.
+enum Plant {
+  PLANT_NONE = 0,
+  PLANT_UNCLIPPED_C = 1,    // a caller's C read over the padded tile
+  PLANT_UNCLIPPED_D = 2,    // a caller's output written over the padded tile
+  PLANT_K_OVERRUN = 3,      // a GEMM reads one K block past its operands
+  PLANT_CAST_ROWS = 4,      // the cast writes 64 rows past its padded block
+  PLANT_SUMSQ_ROW = 5,      // the norm pass reads one row past G
+  PLANT_REDUCE_TAIL = 6,    // a shard reduction runs one block past its parts
+};
+bool plant_mistake(Plan& pl, const unsigned char* ws, size_t ws_bytes, int plant) {
+  auto in_ws = [&](const void* p) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), w = reinterpret_cast<uintptr_t>(ws);
+    return a >= w && a < w + ws_bytes;
+  };
+  for (Stage& st : pl.stages) {
+    unsigned char* t = pl.table.data() + st.off;
+    if (st.kind == Stage::GEMM) {
+      GemmDesc* d = reinterpret_cast<GemmDesc*>(t);
+      for (int i = 0; i < st.count; ++i) {
+        GemmDesc& g = d[i];
+        if (plant == PLANT_UNCLIPPED_C && g.C && !g.c_is_bt && !in_ws(g.C) &&
+            (g.valid_m < g.M || g.valid_n < g.N)) {
+          g.valid_m = g.M;
+          g.valid_n = g.N;
+          return true;
+        }
+        if (plant == PLANT_UNCLIPPED_D && !in_ws(g.D) && (g.valid_m < g.M || g.valid_n < g.N)) {
+          g.valid_m = g.M;
+          g.valid_n = g.N;
+          return true;
+        }
+        if (plant == PLANT_K_OVERRUN) {
+          g.K += gemm_k_multiple();
+          return true;
+        }
+      }
+    } else if (st.kind == Stage::CAST && plant == PLANT_CAST_ROWS && st.count > 0) {
+      NormDesc* d = reinterpret_cast<NormDesc*>(t);
+      const int old = d[0].tiles;
+      d[0].pm += CAST_TILE;
+      d[0].tiles = ceil_div(d[0].pm, CAST_TILE) * d[0].tiles_n;
+      for (int i = 1; i < st.count; ++i) d[i].tile_begin += d[0].tiles - old;
+      st.total += d[0].tiles - old;
+      return true;
+    } else if (st.kind == Stage::SUMSQ && plant == PLANT_SUMSQ_ROW && st.count > 0) {
+      NormDesc* d = reinterpret_cast<NormDesc*>(t);
+      d[0].m += 1;
+      return true;
+    } else if (st.kind == Stage::REDUCE && plant == PLANT_REDUCE_TAIL && st.count > 0) {
+      ReduceDesc* d = reinterpret_cast<ReduceDesc*>(t);
+      d[0].elems += REDUCE_ELEMS;
+      return true;
+    }
+  }
+  return false;
 }
 
 // ---------------------------------------------------------------- timing
@@ -771,9 +1062,14 @@ ns_status run_batched(const ns_matrix* mats, int count, ns_backend be, const ns_
   if (!ws || ws_bytes < sizing.total) return NS_ERR_WORKSPACE;
   s = check_device();
   if (s != NS_OK) return s;
+  if (reinterpret_cast<uintptr_t>(ws) % ALIGN) return NS_ERR_WORKSPACE;
   Plan pl;
-  build_plan(pl, mats, count, be, *p, static_cast<unsigned char*>(ws), shards, muon, beta, lr);
-  return run_plan(pl, static_cast<unsigned char*>(ws), static_cast<hipStream_t>(stream));
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  build_plan(pl, mats, count, be, *p, w, shards, muon, beta, lr);
+  Bounds bounds;
+  allow_buffers(bounds, pl, w, mats, count);
+  if (!validate_plan(pl, w, bounds)) return NS_ERR_INTERNAL;
+  return run_plan(pl, w, static_cast<hipStream_t>(stream));
 }
 
 std::string g_info;
@@ -790,6 +1086,7 @@ NS_API const char* ns_status_string(ns_status s) {
     case NS_ERR_UNSUPPORTED: return "NS_ERR_UNSUPPORTED";
     case NS_ERR_WORKSPACE: return "NS_ERR_WORKSPACE";
     case NS_ERR_HIP: return "NS_ERR_HIP";
+    case NS_ERR_INTERNAL: return "NS_ERR_INTERNAL";
   }
   return "NS_ERR_UNKNOWN";
 }
@@ -1104,8 +1401,147 @@ NS_API ns_status ns_gemm_nt(const void* a, const void* b, const void* c, void* d
   return NS_OK;
 }
 
+// Grouped kernel-level products with every descriptor option (see
+// ns_gemm_problem in ns.h). Checks mirror what the kernel's epilogue paths
+// honour, so an option the kernel would silently ignore is refused.
+namespace nsmi {
+namespace {
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+ns_status grouped_desc(const ns_gemm_problem& q, GemmDesc& g) {
+  const int T = gemm_tile();
+  if (!q.a || !q.b || !q.d) return NS_ERR_INVALID_ARG;
+  if (q.M < T || q.N < T || q.K < gemm_k_multiple() || q.M % T || q.N % T ||
+      q.K % gemm_k_multiple() || q.M > NS_MAX_DIM || q.N > NS_MAX_DIM || q.K > NS_MAX_DIM)
+    return NS_ERR_INVALID_ARG;
+  if (!dtype_ok(q.d_dtype) || (q.c && !dtype_ok(q.c_dtype))) return NS_ERR_INVALID_ARG;
+  if (q.ldd < q.N || (q.c && q.ldc < q.N)) return NS_ERR_INVALID_ARG;
+  if (q.valid_m < 0 || q.valid_m > q.M || q.valid_n < 0 || q.valid_n > q.N || q.diag_n < 0 ||
+      q.diag_n > std::min(q.M, q.N))
+    return NS_ERR_INVALID_ARG;
+  if (!std::isfinite(q.alpha) || !std::isfinite(q.beta) || !std::isfinite(q.gamma) ||
+      !std::isfinite(q.delta))
+    return NS_ERR_INVALID_ARG;
+  if (!aligned16(q.a) || !aligned16(q.b)) return NS_ERR_INVALID_ARG;
+  if ((q.c_pairs && q.c && q.ldc % 32) || (q.d_pairs && q.ldd % 32)) return NS_ERR_INVALID_ARG;
+  const bool fold = q.c_is_bt != 0;
+  if (fold && (!q.c || q.M > q.K || q.alpha == 0.f)) return NS_ERR_INVALID_ARG;
+  const bool full16 = q.d_dtype == NS_DT_F16 && q.valid_m == q.M && q.valid_n == q.N &&
+                      q.ldd % 8 == 0 && aligned16(q.d);
+  if (q.symmetric) {
+    if (q.M != q.N || !full16 || q.dt) return NS_ERR_INVALID_ARG;
+    if (q.c && !fold && (q.c_dtype != NS_DT_F16 || q.ldc % 8 || !aligned16(q.c)))
+      return NS_ERR_INVALID_ARG;
+    if (q.d2 && !aligned16(q.d2)) return NS_ERR_INVALID_ARG;
+  } else {
+    if (q.d2) return NS_ERR_INVALID_ARG;   // second output only in symmetric mode
+    if (q.dt && (!full16 || !aligned16(q.dt) || (q.c && !fold && q.c_dtype != NS_DT_F16)))
+      return NS_ERR_INVALID_ARG;
+  }
+  g = gemm(static_cast<const _Float16*>(q.a), static_cast<const _Float16*>(q.b),
+           static_cast<const _Float16*>(q.c), q.d, static_cast<_Float16*>(q.d2),
+           static_cast<_Float16*>(q.dt), q.M, q.N, q.K, q.ldd, q.valid_m, q.valid_n, q.diag_n,
+           out_code(q.d_dtype), q.symmetric != 0, q.alpha, q.c ? q.beta : 0.f, q.gamma,
+           q.delta);
+  g.C = q.c;
+  g.ldc = static_cast<int>(q.c ? q.ldc : q.N);
+  g.c_type = out_code(q.c ? q.c_dtype : NS_DT_F16);
+  g.c_is_bt = fold ? 1 : 0;
+  g.a_pairs = q.a_pairs ? 1 : 0;
+  g.b_pairs = q.b_pairs ? 1 : 0;
+  g.c_pairs = q.c_pairs ? 1 : 0;
+  g.d_pairs = q.d_pairs ? 1 : 0;
+  return NS_OK;
+}
+}  // namespace
+}  // namespace nsmi
+
+NS_API ns_status ns_gemm_grouped_workspace_size(int count, size_t* bytes) {
+  if (!bytes || count < 1) return NS_ERR_INVALID_ARG;
+  *bytes = align_up(static_cast<size_t>(count) * sizeof(GemmDesc) + 64);
+  return NS_OK;
+}
+
+NS_API ns_status ns_gemm_grouped(const ns_gemm_problem* probs, int count, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (count < 0 || (count > 0 && !probs)) return NS_ERR_INVALID_ARG;
+  if (count == 0) return NS_OK;
+  Probs v;
+  for (int i = 0; i < count; ++i) {
+    GemmDesc g{};
+    const ns_status s = grouped_desc(probs[i], g);
+    if (s != NS_OK) return s;
+    v.d.push_back(g);
+  }
+  size_t need = 0;
+  ns_gemm_grouped_workspace_size(count, &need);
+  if (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % ALIGN) return NS_ERR_WORKSPACE;
+  const ns_status s = check_device();
+  if (s != NS_OK) return s;
+  // the stage planner's order: longer K first, then more tiles
+  std::stable_sort(v.d.begin(), v.d.end(), [](const GemmDesc& a, const GemmDesc& b) {
+    if (a.K != b.K) return a.K > b.K;
+    return a.tiles > b.tiles;
+  });
+  int begin = 0;
+  for (auto& d : v.d) {
+    d.tile_begin = begin;
+    begin += d.tiles;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (upload(ws, v.d.data(), v.d.size() * sizeof(GemmDesc), st) != hipSuccess) return NS_ERR_HIP;
+  if (launch_gemm(static_cast<const GemmDesc*>(ws), count, begin, st) != hipSuccess)
+    return NS_ERR_HIP;
+  return NS_OK;
+}
+
 NS_API ns_status ns_syrk(const void* x, int64_t s, int64_t l, void* r, void* ws,
                          size_t ws_bytes, void* stream) {
   if (!x || !r) return NS_ERR_INVALID_ARG;
   return ns_gemm_nt(x, x, nullptr, r, s, s, l, 1.f, 0.f, 0.f, 1, ws, ws_bytes, stream);
+}
+
+// --------------------------------------------------------------- self-check
+
+NS_API ns_status ns_plan_check(ns_check_entry entry, const void* mats, int count,
+                               ns_backend backend, int shards, const ns_params* params,
+                               void* ws, size_t ws_bytes, int plant, char* msg,
+                               size_t msg_len) {
+  if (msg && msg_len) msg[0] = 0;
+  std::vector<ns_matrix> muon_mats;
+  const ns_matrix* m = nullptr;
+  const ns_muon_matrix* muon = nullptr;
+  ns_status s = NS_OK;
+  if (entry == NS_CHECK_MUON) {
+    muon = static_cast<const ns_muon_matrix*>(mats);
+    s = muon_matrices(muon, count, 0.9f, 0.02f, muon_mats, true);
+    m = muon_mats.data();
+    backend = NS_GRAM;
+    shards = 1;
+  } else if (entry == NS_CHECK_SHARDED) {
+    m = static_cast<const ns_matrix*>(mats);
+    if (count != 1 || !m) return NS_ERR_INVALID_ARG;
+    s = check_shards(*m, shards);
+    backend = NS_GRAM;
+  } else if (entry == NS_CHECK_BATCHED) {
+    m = static_cast<const ns_matrix*>(mats);
+    shards = 1;
+  } else {
+    return NS_ERR_INVALID_ARG;
+  }
+  if (s == NS_OK) s = check_call(m, count, backend, params);
+  if (s != NS_OK) return s;
+  if (count == 0) return NS_OK;
+  if (!ws || reinterpret_cast<uintptr_t>(ws) % ALIGN) return NS_ERR_WORKSPACE;
+  Plan pl;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  build_plan(pl, m, count, backend, *params, w, shards, muon, 0.9f, 0.02f);
+  if (ws_bytes == 0) ws_bytes = pl.total;
+  if (ws_bytes < pl.total) return NS_ERR_WORKSPACE;
+  if (plant != PLANT_NONE && !plant_mistake(pl, w, ws_bytes, plant)) return NS_ERR_UNSUPPORTED;
+  Bounds bounds;
+  allow_buffers(bounds, pl, w, m, count);
+  if (validate_plan(pl, w, bounds)) return NS_OK;
+  if (msg && msg_len) std::snprintf(msg, msg_len, "%s", bounds.err.c_str());
+  return NS_ERR_INTERNAL;
 }

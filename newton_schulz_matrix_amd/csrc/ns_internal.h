@@ -126,7 +126,18 @@ struct ReduceDesc {
   int blocks;
 };
 
+// Descriptor tables reach the device as kernel arguments: each launch of
+// the fill kernel carries TABLE_CHUNK bytes and stores them at `dst`. No
+// host staging buffer outlives the call, so a call can be captured into a
+// HIP graph and replayed (the bytes are part of the captured launch).
+constexpr int TABLE_CHUNK = 2048;
+struct TableChunk {
+  unsigned char bytes[TABLE_CHUNK];
+};
+
 // Launchers (all enqueue on `stream`; return hipSuccess or the launch error).
+hipError_t launch_table_fill(unsigned char* dst, const TableChunk& chunk, int bytes,
+                             hipStream_t stream);
 hipError_t launch_sumsq(const NormDesc* descs, int count, int total_chunks,
                         hipStream_t stream);
 hipError_t launch_norm_finalize(const NormDesc* descs, int count,
