@@ -75,3 +75,23 @@ def test_pages_flop_count():
     assert abs(want / 1e12 - 59.547) < 1e-3
     # restart 0 and out-of-range indices are no restarts
     assert bench.pages_flops([(64, 64)], 5, (0,)) == closed(64, 64, 0, 5 + 4 + 8)
+
+
+def test_oracle_flop_count():
+    """fp64 flops of one oracle gram call: full products everywhere, so the
+    Gram R = X X^T at 2 s^2 l (once plus once per effective restart), the
+    Q X products at 2 s^2 l, and 14 s^3 products for five steps with a
+    restart before step 2 (5 Z, 3 Q updates, 3 recurrences of two), 11 for
+    restarts [1, 3]."""
+    s, l = 256, 1024
+    assert bench.oracle_gram_flops(s, l, 5, (2,)) == 2 * (2 * s * s * l) * 2 + 14 * 2 * s ** 3
+    assert bench.oracle_gram_flops(s, l, 5, (1, 3)) == 3 * (2 * s * s * l) * 2 + 11 * 2 * s ** 3
+    assert bench.oracle_gram_flops(s, l, 5, ()) == 1 * (2 * s * s * l) * 2 + 17 * 2 * s ** 3
+
+
+def test_target_is_stated_on_work_done():
+    import workloads as W
+    t = bench.target_status(1086.0, 28, W.WORKLOADS[4], 37.0, 5)
+    assert abs(t["pct_fp16_peak_work_done"] - 43.44) < 1e-6
+    assert t["met"] is False and t["target_pct_fp16_peak"] == 50.0
+    assert "value_over_target" not in json.dumps(t)
