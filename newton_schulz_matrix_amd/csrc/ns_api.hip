@@ -1415,10 +1415,11 @@ ns_status grouped_desc(const ns_gemm_problem& q, GemmDesc& g) {
       q.K % gemm_k_multiple() || q.M > NS_MAX_DIM || q.N > NS_MAX_DIM || q.K > NS_MAX_DIM)
     return NS_ERR_INVALID_ARG;
   if (!dtype_ok(q.d_dtype) || (q.c && !dtype_ok(q.c_dtype))) return NS_ERR_INVALID_ARG;
-  if (q.ldd < q.N || (q.c && q.ldc < q.N)) return NS_ERR_INVALID_ARG;
   if (q.valid_m < 0 || q.valid_m > q.M || q.valid_n < 0 || q.valid_n > q.N || q.diag_n < 0 ||
       q.diag_n > std::min(q.M, q.N))
     return NS_ERR_INVALID_ARG;
+  // rows of d (and of an unfolded c) hold at least the stored block's width
+  if (q.ldd < q.valid_n || (q.c && !q.c_is_bt && q.ldc < q.valid_n)) return NS_ERR_INVALID_ARG;
   if (!std::isfinite(q.alpha) || !std::isfinite(q.beta) || !std::isfinite(q.gamma) ||
       !std::isfinite(q.delta))
     return NS_ERR_INVALID_ARG;
