@@ -166,6 +166,24 @@ ns_status ns_batched(const ns_matrix* mats, int count, ns_backend backend,
                      const ns_params* params, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* ns_batched without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments (minus the workspace),
+ * results and errors as ns_batched, each output bitwise equal to it; the
+ * workspace is instead a static device array of NS_NOALLOC_SCRATCH_BYTES
+ * bytes inside the library, one per device, held until the process ends.
+ * A call whose ns_workspace_size exceeds that returns NS_ERR_WORKSPACE
+ * before any device work. The call allocates no device memory and no
+ * pinned host memory, creates no events and never times its launches (its
+ * first call on a device resolves the array's address there once).
+ * Every call on a device shares that device's array, which keeps the last
+ * call's contents (nothing in it needs clearing: each call writes all it
+ * reads), so calls that overlap on one device race: order them on one
+ * stream. */
+#define NS_NOALLOC_SCRATCH_BYTES (128u << 20)
+ns_status ns_batched_noalloc(const ns_matrix* mats, int count, ns_backend backend,
+                             const ns_params* params, void* stream);
+
 /* Column-sharded Gram NS on one matrix, the tensor-parallel route of the
  * pages (Newton-Schulz reference page, section "Gram 空间 NS": R is a sum of
  * local Gram matrices, so TP is exact through one all-reduce; article page,

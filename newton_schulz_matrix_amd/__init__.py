@@ -139,6 +139,7 @@ def library() -> ctypes.CDLL:
             "ns_direct": [M, P, vp, sz, vp],
             "ns_gram": [M, P, vp, sz, vp],
             "ns_batched": [M, ctypes.c_int, ctypes.c_int, P, vp, sz, vp],
+            "ns_batched_noalloc": [M, ctypes.c_int, ctypes.c_int, P, vp],
             "ns_gram_sharded_workspace_size": [M, ctypes.c_int, P, ctypes.POINTER(sz)],
             "ns_gram_sharded": [M, ctypes.c_int, P, vp, sz, vp],
             "ns_muon_workspace_size": [ctypes.POINTER(_MuonMatrix), ctypes.c_int, P,
@@ -339,6 +340,29 @@ def ns_batched(Gs: List, backend: str = "gram",
     _check(lib.ns_batched(mats, len(Gs), BACKENDS[backend], ctypes.byref(p),
                           workspace.data_ptr(), workspace.numel(), _stream_ptr(Gs[0])),
            "ns_batched")
+    return outs
+
+
+NS_NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def ns_batched_noalloc(Gs: List, outs: List, backend: str = "gram",
+                       coefficients=POLAR_EXPRESS_COEFFICIENTS,
+                       restart_iterations: Iterable[int] = DEFAULT_RESTARTS,
+                       eps: float = DEFAULT_EPS) -> List:
+    """ns_batched with the library's static device scratch as the workspace
+    (nothing is allocated; the caller passes the outputs). Calls that
+    overlap on one device race; see ns_batched_noalloc in ns.h."""
+    if len(Gs) != len(outs):
+        raise ValueError("one output per input")
+    if len(Gs) == 0:
+        return outs
+    mats = (_Matrix * len(Gs))()
+    for i, (G, O) in enumerate(zip(Gs, outs)):
+        mats[i] = _matrix(_device_tensor(G, "G"), _device_tensor(O, "out"))
+    p, keep = _params(coefficients, restart_iterations, eps)
+    _check(library().ns_batched_noalloc(mats, len(Gs), BACKENDS[backend], ctypes.byref(p),
+                                        _stream_ptr(Gs[0])), "ns_batched_noalloc")
     return outs
 
 

@@ -989,10 +989,11 @@ hipError_t timed(bool on, bool gemm_kind, double work, hipStream_t stream, F lau
   return e;
 }
 
-ns_status run_plan(const Plan& pl, unsigned char* ws, hipStream_t stream) {
+ns_status run_plan(const Plan& pl, unsigned char* ws, hipStream_t stream,
+                   bool allow_timing = true) {
   unsigned char* table = ws + pl.table_off;
   if (upload(table, pl.table.data(), pl.table.size(), stream) != hipSuccess) return NS_ERR_HIP;
-  const bool on = timing_on();
+  const bool on = allow_timing && timing_on();
   for (const Stage& st : pl.stages) {
     hipError_t e = hipSuccess;
     switch (st.kind) {
@@ -1053,7 +1054,8 @@ ns_status check_shards(const ns_matrix& a, int shards) {
 
 ns_status run_batched(const ns_matrix* mats, int count, ns_backend be, const ns_params* p,
                       void* ws, size_t ws_bytes, void* stream, int shards = 1,
-                      const ns_muon_matrix* muon = nullptr, float beta = 0.f, float lr = 0.f) {
+                      const ns_muon_matrix* muon = nullptr, float beta = 0.f, float lr = 0.f,
+                      bool allow_timing = true) {
   ns_status s = check_call(mats, count, be, p);
   if (s != NS_OK) return s;
   if (count == 0) return NS_OK;
@@ -1069,7 +1071,7 @@ ns_status run_batched(const ns_matrix* mats, int count, ns_backend be, const ns_
   Bounds bounds;
   allow_buffers(bounds, pl, w, mats, count);
   if (!validate_plan(pl, w, bounds)) return NS_ERR_INTERNAL;
-  return run_plan(pl, w, static_cast<hipStream_t>(stream));
+  return run_plan(pl, w, static_cast<hipStream_t>(stream), allow_timing);
 }
 
 std::string g_info;
@@ -1545,4 +1547,53 @@ NS_API ns_status ns_plan_check(ns_check_entry entry, const void* mats, int count
   if (validate_plan(pl, w, bounds)) return NS_OK;
   if (msg && msg_len) std::snprintf(msg, msg_len, "%s", bounds.err.c_str());
   return NS_ERR_INTERNAL;
+}
+
+// ------------------------------------------------------ no-allocation entry
+// ns_batched for callers that cannot allocate device memory: the workspace
+// is this file-scope device array. The host-side name `scratch` is only a
+// stand-in for the symbol; each device's copy lives at its own address,
+// resolved once per device with hipGetSymbolAddress (with that device
+// current), and only that address is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[NS_NOALLOC_SCRATCH_BYTES];
+
+namespace nsmi {
+namespace {
+std::mutex g_scratch_mu;
+std::map<int, unsigned char*> g_scratch;   // device -> address of its `scratch`
+
+ns_status scratch_address(unsigned char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return NS_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch.find(dev);
+  if (it == g_scratch.end()) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return NS_ERR_HIP;
+    }
+    it = g_scratch.emplace(dev, static_cast<unsigned char*>(p)).first;
+  }
+  *out = it->second;
+  return NS_OK;
+}
+}  // namespace
+}  // namespace nsmi
+
+NS_API ns_status ns_batched_noalloc(const ns_matrix* mats, int count, ns_backend backend,
+                                    const ns_params* params, void* stream) {
+  ns_status s = check_call(mats, count, backend, params);
+  if (s != NS_OK) return s;
+  if (count == 0) return NS_OK;
+  Plan sizing;
+  build_plan(sizing, mats, count, backend, *params, nullptr);
+  if (sizing.total > NS_NOALLOC_SCRATCH_BYTES) return NS_ERR_WORKSPACE;
+  s = check_device();
+  if (s != NS_OK) return s;
+  unsigned char* ws = nullptr;
+  s = scratch_address(&ws);
+  if (s != NS_OK) return s;
+  return run_batched(mats, count, backend, params, ws, NS_NOALLOC_SCRATCH_BYTES, stream, 1,
+                     nullptr, 0.f, 0.f, /*allow_timing=*/false);
 }
