@@ -311,8 +311,11 @@ ns_status ns_gemm_nt(const void* a, const void* b, const void* c, void* d,
  * M, N multiples of 256, K a multiple of 128, all sides <= NS_MAX_DIM.
  * Problems share one launch, ordered as the iteration's stages order them
  * (longer K first); the workspace holds the launch descriptors
- * (ns_gemm_grouped_workspace_size). Asynchronous on `stream`; errors as
- * for every entry point. */
+ * (ns_gemm_grouped_workspace_size). tile_edge selects the kernel: 256 (the
+ * 256 x 256 tile kernel), 64 (the 64 x 64 tile kernel the stages use when
+ * they have fewer than 64 tiles of 256 x 256; it gives the same bits), or
+ * 0 (that same rule). Asynchronous on `stream`; errors as for every entry
+ * point. */
 typedef struct {
   const void* a;
   const void* b;
@@ -328,8 +331,8 @@ typedef struct {
   float alpha, beta, gamma, delta;
 } ns_gemm_problem;
 ns_status ns_gemm_grouped_workspace_size(int count, size_t* bytes);
-ns_status ns_gemm_grouped(const ns_gemm_problem* probs, int count, void* ws, size_t ws_bytes,
-                          void* stream);
+ns_status ns_gemm_grouped(const ns_gemm_problem* probs, int count, int tile_edge, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /* Host-side self-check of a call's launch plan (testing and diagnostics;
  * needs no device, launches nothing and dereferences no pointer). Builds the

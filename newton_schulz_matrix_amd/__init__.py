@@ -150,7 +150,8 @@ def library() -> ctypes.CDLL:
             "ns_gemm_nt": [vp, vp, vp, vp, i64, i64, i64, ctypes.c_float, ctypes.c_float,
                            ctypes.c_float, ctypes.c_int, vp, sz, vp],
             "ns_gemm_grouped_workspace_size": [ctypes.c_int, ctypes.POINTER(sz)],
-            "ns_gemm_grouped": [ctypes.POINTER(_GemmProblem), ctypes.c_int, vp, sz, vp],
+            "ns_gemm_grouped": [ctypes.POINTER(_GemmProblem), ctypes.c_int, ctypes.c_int, vp, sz,
+                                vp],
             "ns_plan_check": [ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, P,
                               vp, sz, ctypes.c_int, ctypes.c_char_p, sz],
         }
@@ -526,7 +527,7 @@ def ns_gemm_nt(A, B, C=None, alpha: float = 1.0, beta: float = 0.0,
     return D
 
 
-def ns_gemm_grouped(problems: List[dict]) -> None:
+def ns_gemm_grouped(problems: List[dict], tile_edge: int = 0) -> None:
     """Products of the grouped GEMM kernel with every descriptor option, in
     one launch (kernel-level testing; see ns_gemm_problem in ns.h).
 
@@ -535,7 +536,8 @@ def ns_gemm_grouped(problems: List[dict]) -> None:
     "c", "d2", "dt", the sizes "M", "N", "K", and optionally "ldc", "ldd"
     (default N), "valid_m", "valid_n" (default M, N), "diag_n" (default 0),
     "symmetric", "c_is_bt", "a_pairs", "b_pairs", "c_pairs", "d_pairs"
-    (default 0), "alpha" (1), "beta", "gamma", "delta" (0)."""
+    (default 0), "alpha" (1), "beta", "gamma", "delta" (0). tile_edge: 256
+    or 64 forces that kernel, 0 picks as the iteration's stages do."""
     if not problems:
         return
     arr = (_GemmProblem * len(problems))()
@@ -564,7 +566,7 @@ def ns_gemm_grouped(problems: List[dict]) -> None:
     _check(lib.ns_gemm_grouped_workspace_size(len(problems), ctypes.byref(nbytes)),
            "ns_gemm_grouped_workspace_size")
     ws = _workspace(nbytes.value, dev)
-    _check(lib.ns_gemm_grouped(arr, len(problems), ws.data_ptr(), ws.numel(),
+    _check(lib.ns_gemm_grouped(arr, len(problems), int(tile_edge), ws.data_ptr(), ws.numel(),
                                _stream_ptr(problems[0]["a"])), "ns_gemm_grouped")
 
 

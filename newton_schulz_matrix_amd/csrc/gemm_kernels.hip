@@ -37,7 +37,16 @@
 //     (row / 4) % 4 so the 16 lanes served per cycle by a 128-bit LDS read
 //     (16 consecutive rows) hit 16 distinct bank groups;
 //   * workgroup ids are remapped so each XCD (8 per MI355X, one L2 each)
-//     works on runs of 32 neighbouring tiles that share operand panels.
+//     works on runs of 32 neighbouring tiles that share operand panels;
+//   * on a diagonal tile of a symmetric product group 0's four waves split
+//     the 128 stored columns of their rows (32 each) rather than two of them
+//     computing the never-stored upper-right quadrant;
+//   * epilogue arithmetic is written out (explicit fused multiply-adds, the
+//     fp32 value held before its conversion), so every code path computing
+//     an element rounds it the same way.
+// A second kernel runs the same products on 64 x 64 tiles, for stages whose
+// few 256 x 256 tiles would leave most of the chip idle; it produces the same
+// bits (see gemm_small_kernel).
 #include "ns_internal.h"
 
 #include <type_traits>
@@ -232,6 +241,16 @@ __device__ __forceinline__ void store_typed(void* p, int64_t k, float v) {
   else gmem(static_cast<uint16_t*>(p))[k] = to_bf16_bits(v);
 }
 
+// The fp32 value of an epilogue is held in a register before it is
+// converted to the output type: otherwise the compiler may fuse the last
+// multiply-add with the conversion (a mixed-precision fma rounding the exact
+// result once to fp16) in some inlined copies and not in others, and rare
+// ties would round differently depending on which copy computed an element.
+__device__ __forceinline__ float fp32_value(float x) {
+  asm("" : "+v"(x));
+  return x;
+}
+
 // MFMA 32x32 output layout: register r of lane l holds row
 // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of each 32x32 block.
 
@@ -263,9 +282,10 @@ __device__ __forceinline__ void epilogue_output_t(const Acc& acc, const Epi& e) 
       for (int r = 0; r < 16; ++r) {
         const int row = rb0 + (r / 4) * 8 + (r % 4);
         float x = e.alpha * a[r];
-        if constexpr (CT >= 0) x += e.beta * c[r];
+        if constexpr (CT >= 0) x = __builtin_fmaf(e.beta, c[r], x);
         if (row == col && col < e.diag_n) x += e.gamma;
-        if (col_ok && row < e.valid_m) store_typed<OT>(e.D, lidx(e.d_pairs, row, col, e.ldd), x);
+        if (col_ok && row < e.valid_m)
+          store_typed<OT>(e.D, lidx(e.d_pairs, row, col, e.ldd), fp32_value(x));
       }
     });
   });
@@ -356,15 +376,18 @@ template <class Cf, int MODE, class Acc>
 __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Float16* S,
                                               float* sdiag, int lane, int wm, int wn,
                                               int m0, int n0, _Float16* T, int ldT,
-                                              _Float16* T2) {
+                                              _Float16* T2, bool half_cols = false) {
   static_assert(Cf::BM == 256 && Cf::BN == 256, "tile-wide staging is 256 x 256");
   constexpr bool SYM = MODE == EPI_SYM_OFFDIAG || MODE == EPI_SYM_DIAG;
   lds_char* const Sl = (lds_char*)(S);
   const int h = lane >> 5;
   static_for<0, Cf::FM>([&](auto I) {
     static_for<0, Cf::FN>([&](auto J) {
+      // group 0 of a diagonal tile computed one 32-column block per wave
+      if (MODE == EPI_SYM_DIAG && half_cols && J > 0) return;
       const floatx16& a = acc[I][J];
-      const int lcol = wn * Cf::WN + J * 32 + (lane & 31);     // tile-local column
+      const int lcol = (MODE == EPI_SYM_DIAG && half_cols ? wn * 32 : wn * Cf::WN) + J * 32 +
+                       (lane & 31);                              // tile-local column
       const int lrow0 = wm * Cf::WM + I * 32;                   // tile-local block row
       const int col = n0 + lcol, rbase = m0 + lrow0;            // global
       uint32_t P[4][2];
@@ -391,11 +414,13 @@ __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Flo
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int row = rbase + g * 8 + h * 4 + q;
+            // fused multiply-adds written out, so that every code path
+            // computing an element rounds it the same way
             float x = e.alpha * a[g * 4 + q];
-            if constexpr (SYM) x += e.beta * c[GG][q];
+            if constexpr (SYM) x = __builtin_fmaf(e.beta, c[GG][q], x);
             if constexpr (MODE == EPI_FULL_C)
-              x += e.beta * static_cast<float>(
-                  gmem(static_cast<const _Float16*>(e.C))[lidx(e.c_pairs, row, col, e.ldc)]);
+              x = __builtin_fmaf(e.beta, static_cast<float>(gmem(static_cast<const _Float16*>(
+                                     e.C))[lidx(e.c_pairs, row, col, e.ldc)]), x);
             v[q] = x;
           }
           if (bdiag) {
@@ -407,6 +432,8 @@ __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Flo
                 if (row == col) sdiag[row - m0] = v[q];
             }
           }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = fp32_value(v[q]);
           P[g][0] = pack_h2(v[0], v[1]);
           P[g][1] = pack_h2(v[2], v[3]);
         });
@@ -465,7 +492,7 @@ __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Flo
           // the second output adds delta on the real diagonal, from fp32
           if (lr >= lc && lr < lc + 8 && m0 + lr < e.diag_n) {
             const int k = lr - lc;
-            const uint16_t hb = __builtin_bit_cast(uint16_t, static_cast<_Float16>(sdiag[lr] + e.delta));
+            const uint16_t hb = __builtin_bit_cast(uint16_t, static_cast<_Float16>(fp32_value(sdiag[lr] + e.delta)));
             const uint32_t w = val[k >> 1];
             val[k >> 1] = (k & 1) ? ((w & 0xffffu) | (static_cast<uint32_t>(hb) << 16))
                                   : ((w & 0xffff0000u) | hb);
@@ -505,6 +532,13 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  // On a diagonal tile of a symmetric product only the lower triangle is
+  // stored (the upper one is its mirror); group 0 (tile rows 0-127) then
+  // needs columns 0-127 only, and its four waves split them (32 columns
+  // each) instead of two of them computing the never-stored upper-right
+  // quadrant: half the MFMAs for group 0, the same value for every element.
+  const bool half_cols = sym && ti == tj && wm == 0;
+  const int bcol0 = half_cols ? wn * 32 : wn * C::WN;   // first column of this wave's blocks
 
   // beta * C taken from the B slices (C == B^T): global row i of C is
   // column k = i of B, so this wave's 32-row block I arrives with K slice
@@ -555,10 +589,9 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
     });
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Fragment register sets: the MFMAs of slice t run on one set while the
-  // fragments of slice t+1 are read into the other.
+  // One fragment register set per wave: a wave reads the next slice's
+  // fragments only in the phase after issuing its MFMAs of the current one.
   half8 fa0[C::KSTEPS][C::FM], fb0[C::KSTEPS][C::FN];
-  half8 fa1[C::KSTEPS][C::FM], fb1[C::KSTEPS][C::FN];
   auto read_frags = [&](const _Float16* SA, const _Float16* SB, auto& fa, auto& fb) {
     static_for<0, C::KSTEPS>([&](auto KS) {
       const int kc = KS * 2 + (lane >> 5);
@@ -567,8 +600,10 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
         fa[KS][I] = *reinterpret_cast<const half8*>(&SA[row * C::BK + ((kc ^ swz(row)) * 8)]);
       });
       static_for<0, C::FN>([&](auto J) {
-        const int row = wn * C::WN + J * 32 + (lane & 31);
-        fb[KS][J] = *reinterpret_cast<const half8*>(&SB[row * C::BK + ((kc ^ swz(row)) * 8)]);
+        if (J == 0 || !half_cols) {
+          const int row = bcol0 + J * 32 + (lane & 31);
+          fb[KS][J] = *reinterpret_cast<const half8*>(&SB[row * C::BK + ((kc ^ swz(row)) * 8)]);
+        }
       });
     });
   };
@@ -582,18 +617,31 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
       });
     });
   };
+  // group 0 of a diagonal tile: one column block per wave
+  auto mfmas_half = [&](auto& fa, auto& fb) {
+    static_for<0, C::KSTEPS>([&](auto KS) {
+      static_for<0, C::FM>([&](auto I) {
+        acc[I][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[KS][I], fb[KS][0], acc[I][0],
+                                                           0, 0, 0);
+      });
+    });
+  };
   // acc[I][J] += rho * C for the 32 rows of block I, read from slice SB:
   // lane l needs rows 8g + 4(l/32) .. +3 (g = 0..3) of column l%32 of block
   // J, i.e. four consecutive k of B row (block J column), 8 bytes.
   auto fold_c = [&](const _Float16* SB, auto I) {
     static_for<0, C::FN>([&](auto J) {
-      const int row = wn * C::WN + J * 32 + (lane & 31);
-      const _Float16* base = SB + row * C::BK + 4 * (lane >> 5);
-      static_for<0, 4>([&](auto G) {
-        const half4 c = *reinterpret_cast<const half4*>(base + ((G ^ swz(row)) * 8));
+      if (J == 0 || !half_cols) {
+        const int row = bcol0 + J * 32 + (lane & 31);
+        const _Float16* base = SB + row * C::BK + 4 * (lane >> 5);
+        static_for<0, 4>([&](auto G) {
+          const half4 c = *reinterpret_cast<const half4*>(base + ((G ^ swz(row)) * 8));
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[I][J][G * 4 + q] += rho * static_cast<float>(c[q]);
-      });
+          for (int q = 0; q < 4; ++q)
+            acc[I][J][G * 4 + q] =
+                __builtin_fmaf(rho, static_cast<float>(c[q]), acc[I][J][G * 4 + q]);
+        });
+      }
     });
   };
   // Ping-pong schedule, one barrier per phase. On every SIMD one wave of
@@ -612,14 +660,18 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto mfma_phase = [&](auto& fa, auto& fb) {
-    mfmas(fa, fb);
+  // HALF: group 0 of a diagonal tile (chosen once per tile, so that the
+  // MFMA stream of a phase stays one straight-line block)
+  auto mfma_phase = [&](auto& fa, auto& fb, auto HALF) {
+    if constexpr (decltype(HALF)::value) mfmas_half(fa, fb);
+    else mfmas(fa, fb);
     __builtin_amdgcn_sched_barrier(0);
   };
   // K is a multiple of STAGES * BK; requests past the last slice re-read the
   // last slice into a stage that is never consumed again.
   const int nk = K / C::BK;
   auto kclamp = [&](int sl) { return min(sl, nk - 1) * C::BK; };
+  auto k_loop = [&](auto HALF) {
   static_for<0, STAGES>([&](auto s) { copy_my(s, kclamp(s)); });
   // only slice 0 is read before the next wait; slices 1-3 keep streaming
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * COPIES) & ~0x0F00);
@@ -631,11 +683,11 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
     for (int kt = 0; kt < nk; kt += STAGES) {
       static_for<0, STAGES>([&](auto U) {
         constexpr int u = U;
-        auto& fa = (u % 2 == 0) ? fa0 : fa1;
-        auto& fb = (u % 2 == 0) ? fb0 : fb1;
-        auto& fan = (u % 2 == 0) ? fa1 : fa0;
-        auto& fbn = (u % 2 == 0) ? fb1 : fb0;
-        mfma_phase(fa, fb);
+        auto& fa = fa0;
+        auto& fb = fb0;
+        auto& fan = fa0;
+        auto& fbn = fb0;
+        mfma_phase(fa, fb, HALF);
         phase_end();
         copy_my(u, kclamp(kt + u + 4));
         read_frags(stA((u + 1) % STAGES), stB((u + 1) % STAGES), fan, fbn);
@@ -649,17 +701,20 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
     for (int kt = 0; kt < nk; kt += STAGES) {
       static_for<0, STAGES>([&](auto U) {
         constexpr int u = U;
-        auto& fa = (u % 2 == 0) ? fa0 : fa1;
-        auto& fb = (u % 2 == 0) ? fb0 : fb1;
+        auto& fa = fa0;
+        auto& fb = fb0;
         if (kt + u >= 1) copy_my((u + 3) % STAGES, kclamp(kt + u + 3));
         read_frags(stA(u), stB(u), fa, fb);
         if (kt / STAGES == fold_round) fold_c(stB(u), std::integral_constant<int, u>{});
         phase_end();
-        mfma_phase(fa, fb);
+        mfma_phase(fa, fb, HALF);
         phase_end();
       });
     }
   }
+  };
+  if (half_cols) k_loop(std::true_type{});
+  else k_loop(std::false_type{});
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));   // trailing copies
   __builtin_amdgcn_s_barrier();
 
@@ -686,7 +741,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
                                         static_cast<_Float16*>(d.D), d.ldd, d.D2);
     else
       epilogue_tile<C, EPI_SYM_DIAG>(acc, e, smem, sdiag, lane, wm, wn, m0, n0, nullptr, 0,
-                                     nullptr);
+                                     nullptr, half_cols);
   } else if (d.out_type == OUT_F16 && d.valid_m == M && d.valid_n == N && row_store_ok &&
              !d.D2 && (!e.C || d.c_type == OUT_F16)) {
     if (e.C)
@@ -698,10 +753,214 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   }
 #endif
 }
+// ------------------------------------------------------------ small tiles
+// The same products on 64 x 64 tiles, for stages with too few 256 x 256
+// tiles to occupy the chip (a single small matrix puts one 256-tile on one
+// CU per stage). Four waves, each owning one 32 x 32 block of
+// v_mfma_f32_32x32x16_f16; a four-stage ring of 64 x 32 operand slices
+// filled by the same buffer-to-LDS copies; per-element epilogue.
+//
+// Every output element is produced exactly as gemm_nt_kernel produces it:
+// the same MFMA over the same 16-wide k steps in the same order, beta * C
+// folded at the same K slice (before the MFMAs of the slice holding the
+// element's row), the same epilogue arithmetic and the same choice of path
+// (symmetric, whole-tile fp16, or clipped typed output). The two kernels
+// are therefore interchangeable per stage, bit for bit.
+constexpr int SM_TILE = 64;
+constexpr int SM_THREADS = 256;
+constexpr int SM_BK = 32;
+constexpr int SM_STAGES = 4;
+constexpr int SM_SLICE = SM_TILE * SM_BK;   // halves per operand slice
+
+// Logical tile of a symmetric problem -> (ti, tj), tj <= ti, rows of the
+// lower triangle in order: tile t = ti (ti + 1) / 2 + tj.
+__device__ __forceinline__ void decode_lower_rows(int t, int& ti, int& tj) {
+  int r = static_cast<int>((sqrtf(8.f * static_cast<float>(t) + 1.f) - 1.f) * 0.5f);
+  while (r * (r + 1) / 2 > t) --r;
+  while ((r + 1) * (r + 2) / 2 <= t) ++r;
+  ti = r;
+  tj = t - r * (r + 1) / 2;
+}
+
+template <int CT>
+__device__ __forceinline__ float load_c(const GemmDesc& d, int64_t i, int64_t j) {
+  return load_typed<CT>(d.C, lidx(d.c_pairs, i, j, d.ldc));
+}
+
+template <int KIND, int OT, int CT>
+__device__ __forceinline__ void small_epilogue(const floatx16& acc, const GemmDesc& d, bool fold,
+                                               int i0, int j0, bool diag_tile) {
+  // KIND: 0 symmetric, 1 whole-tile fp16, 2 clipped typed output
+  const int lane = threadIdx.x & 63;
+  const int j = j0 + (lane & 31);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = i0 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+    if constexpr (KIND == 2) {
+      if (i >= d.valid_m || j >= d.valid_n) continue;
+    }
+    float x = d.alpha * acc[r];
+    if (!fold && d.C) {
+      // the symmetric path reads C at the transposed position, as the
+      // 256-tile kernel does (C is symmetric there)
+      if constexpr (KIND == 2) x = __builtin_fmaf(d.beta, load_c<CT>(d, i, j), x);
+      else if constexpr (KIND == 0) x = __builtin_fmaf(d.beta, load_c<OUT_F16>(d, j, i), x);
+      else x = __builtin_fmaf(d.beta, load_c<OUT_F16>(d, i, j), x);
+    }
+    const bool on_diag = i == j && j < d.diag_n;
+    if constexpr (KIND == 2) {
+      if (on_diag) x += d.gamma;
+      store_typed<OT>(d.D, lidx(d.d_pairs, i, j, d.ldd), fp32_value(x));
+    } else {
+      if (d.gamma != 0.f && on_diag) x += d.gamma;
+      x = fp32_value(x);
+      const _Float16 h = static_cast<_Float16>(x);
+      _Float16* D = static_cast<_Float16*>(d.D);
+      if constexpr (KIND == 0) {
+        // lower triangle only on diagonal tiles; every stored element is
+        // also stored at its mirror position, as is the second output
+        if (diag_tile && j > i) continue;
+        gmem(D)[lidx(d.d_pairs, i, j, d.ldd)] = h;
+        gmem(D)[lidx(d.d_pairs, j, i, d.ldd)] = h;
+        if (d.D2) {
+          const _Float16 h2 = (i == j && i < d.diag_n)
+                                  ? static_cast<_Float16>(fp32_value(x + d.delta)) : h;
+          gmem(d.D2)[lidx(d.d_pairs, i, j, d.N)] = h2;
+          gmem(d.D2)[lidx(d.d_pairs, j, i, d.N)] = h2;
+        }
+      } else {
+        gmem(D)[lidx(d.d_pairs, i, j, d.ldd)] = h;
+        if (d.DT) gmem(d.DT)[lidx(d.d_pairs, j, i, d.M)] = h;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(SM_THREADS) void gemm_small_kernel(
+    const GemmDesc* __restrict__ descs, int count, int total_tiles) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ __attribute__((aligned(1024))) _Float16 smem[SM_STAGES * 2 * SM_SLICE];
+  auto stA = [&](int s) { return smem + s * 2 * SM_SLICE; };
+  auto stB = [&](int s) { return smem + s * 2 * SM_SLICE + SM_SLICE; };
+  const int t_logical = blockIdx.x;
+  const int p = find_problem(descs, count, t_logical);
+  const GemmDesc& d = descs[p];
+  const int t = t_logical - d.tile_begin;
+  const int K = d.K;
+  const bool sym = d.symmetric != 0;
+  int ti, tj;
+  if (sym) decode_lower_rows(t, ti, tj);
+  else {
+    ti = t / d.tiles_n;
+    tj = t - ti * d.tiles_n;
+  }
+  const int m0 = ti * SM_TILE, n0 = tj * SM_TILE;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool fold = d.c_is_bt != 0;
+  const float rho = fold ? d.beta / d.alpha : 0.f;
+  const int fold_slice = (m0 + 32 * wm) / SM_BK;   // this wave's rows arrive with this K slice
+  floatx16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+
+  // copies: wave w fills rows 16 w .. 16 w + 15 of the A and of the B slice
+  const uint32_t panel = static_cast<uint32_t>(SM_TILE) * K * 2u;
+  const i32x4 rA = make_rsrc(d.A + static_cast<int64_t>(m0) * K, panel);
+  const i32x4 rB = make_rsrc(d.B + static_cast<int64_t>(n0) * K, panel);
+  const int row = wave * 16 + lane / 4;
+  const int col = ((lane % 4) ^ swz(row)) * 8;
+  const uint32_t offA = static_cast<uint32_t>(d.a_pairs ? (row >> 1) * 2 * K + (row & 1) * 32 + col
+                                                        : row * K + col) * 2u;
+  const uint32_t offB = static_cast<uint32_t>(d.b_pairs ? (row >> 1) * 2 * K + (row & 1) * 32 + col
+                                                        : row * K + col) * 2u;
+  const uint32_t kbA = d.a_pairs ? 4u : 2u, kbB = d.b_pairs ? 4u : 2u;
+  const int nk = K / SM_BK;
+  auto copy_slice = [&](int s, int sl) {
+    const uint32_t k0 = static_cast<uint32_t>(min(sl, nk - 1) * SM_BK);
+    lds_copy16(rA, lds_addr_of(stA(s) + wave * 512), offA, k0 * kbA);
+    lds_copy16(rB, lds_addr_of(stB(s) + wave * 512), offB, k0 * kbB);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  static_for<0, SM_STAGES - 1>([&](auto s) { copy_slice(s, s); });
+  half8 fa[2], fb[2];
+  for (int kt = 0; kt < nk; kt += SM_STAGES) {
+    static_for<0, SM_STAGES>([&](auto U) {
+      constexpr int u = U;
+      const int sl = kt + u;
+      // own copies of slice sl done (two later slices may stay in flight),
+      // then every wave's
+      __builtin_amdgcn_s_waitcnt(vmcnt_wait(4) & ~0x0F00);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      copy_slice((u + 3) % SM_STAGES, sl + 3);   // the stage of slice sl - 1, read by now
+      const _Float16* SA = stA(u);
+      const _Float16* SB = stB(u);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int kc = ks * 2 + (lane >> 5);
+        const int ra = wm * 32 + (lane & 31), rb = wn * 32 + (lane & 31);
+        fa[ks] = *reinterpret_cast<const half8*>(&SA[ra * SM_BK + ((kc ^ swz(ra)) * 8)]);
+        fb[ks] = *reinterpret_cast<const half8*>(&SB[rb * SM_BK + ((kc ^ swz(rb)) * 8)]);
+      }
+      if (fold && sl == fold_slice) {
+        const int rb = wn * 32 + (lane & 31);
+        const _Float16* base = SB + rb * SM_BK + 4 * (lane >> 5);
+        static_for<0, 4>([&](auto G) {
+          const half4 c = *reinterpret_cast<const half4*>(base + ((G ^ swz(rb)) * 8));
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[G * 4 + q] = __builtin_fmaf(rho, static_cast<float>(c[q]), acc[G * 4 + q]);
+        });
+      }
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[0], fb[0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[1], fb[1], acc, 0, 0, 0);
+    });
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));   // trailing copies
+
+  const int i0 = m0 + wm * 32, j0 = n0 + wn * 32;
+  // the path gemm_nt_kernel takes for this descriptor
+  const bool row_store_ok =
+      (d.ldd % 8 == 0) && (reinterpret_cast<uintptr_t>(d.D) % 16 == 0);
+  const bool c_unfolded_f16 = fold || !d.C || d.c_type == OUT_F16;
+  if (sym) {
+    small_epilogue<0, OUT_F16, OUT_F16>(acc, d, fold, i0, j0, ti == tj);
+  } else if (d.out_type == OUT_F16 && d.valid_m == d.M && d.valid_n == d.N && row_store_ok &&
+             !d.D2 && c_unfolded_f16) {
+    small_epilogue<1, OUT_F16, OUT_F16>(acc, d, fold, i0, j0, false);
+  } else {
+    const int ct = (fold || !d.C) ? -1 : d.c_type;
+#define NSMI_SMALL_OUT(OT)                                                            \
+    if (d.out_type == OT) {                                                          \
+      if (ct == OUT_F16) small_epilogue<2, OT, OUT_F16>(acc, d, fold, i0, j0, false); \
+      else if (ct == OUT_F32) small_epilogue<2, OT, OUT_F32>(acc, d, fold, i0, j0, false); \
+      else if (ct == OUT_BF16) small_epilogue<2, OT, OUT_BF16>(acc, d, fold, i0, j0, false); \
+      else small_epilogue<2, OT, -1>(acc, d, fold, i0, j0, false);                     \
+    }
+    NSMI_SMALL_OUT(OUT_F16)
+    NSMI_SMALL_OUT(OUT_F32)
+    NSMI_SMALL_OUT(OUT_BF16)
+#undef NSMI_SMALL_OUT
+  }
+#endif
+}
+
 }  // namespace
 
 int gemm_tile() { return MainCfg::BM; }
 int gemm_k_multiple() { return STAGES * MainCfg::BK; }
+
+int gemm_small_tile() { return SM_TILE; }
+
+hipError_t launch_gemm_small(const GemmDesc* descs, int count, int total_tiles,
+                             hipStream_t stream) {
+  if (total_tiles <= 0 || count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_small_kernel, dim3(total_tiles), dim3(SM_THREADS), 0, stream, descs,
+                     count, total_tiles);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(const GemmDesc* descs, int count, int total_tiles,
                        hipStream_t stream) {

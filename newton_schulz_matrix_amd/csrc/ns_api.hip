@@ -28,6 +28,8 @@ namespace nsmi {
 namespace {
 
 constexpr size_t ALIGN = 256;
+// GEMM stages with fewer 256 x 256 tiles than this run on 64 x 64 tiles.
+constexpr int SMALL_STAGE_TILES = 64;
 inline size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
 inline int64_t pad_dim(int64_t x) { return (x + PAD - 1) / PAD * PAD; }
 inline int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
@@ -62,13 +64,66 @@ ns_status check_device() {
 }
 
 // ---------------------------------------------------------------- upload
-// Descriptor tables are copied into the workspace by fill-kernel launches
-// whose arguments carry the bytes (TABLE_CHUNK per launch). Nothing on the
-// host has to stay alive after the call returns, no host memory is
-// allocated, and a call made under HIP graph capture records only kernel
-// launches, so replaying the graph rewrites the same table.
+// Descriptor tables reach the workspace in one of two ways:
+//   * an asynchronous copy from a pinned host staging ring (one copy per
+//     call; a slot is reused only after the copy recorded on it has
+//     completed), for ordinary calls;
+//   * fill-kernel launches whose arguments carry the bytes (TABLE_CHUNK per
+//     launch), when the stream is being captured into a HIP graph (the
+//     bytes then live in the captured launches, and every replay rewrites
+//     the same table) and for the no-allocation entry point (no pinned
+//     memory is ever allocated on that path).
 
-hipError_t upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+struct Slot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+constexpr int RING = 8;
+struct Ring {
+  Slot slot[RING];
+  int next = 0;
+};
+std::mutex g_up_mu;
+std::map<int, Ring> g_rings;
+
+hipError_t upload_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_up_mu);
+  Ring& ring = g_rings[dev];
+  Slot& s = ring.slot[ring.next];
+  ring.next = (ring.next + 1) % RING;
+  if (s.pending) {
+    e = hipEventSynchronize(s.ev);
+    if (e != hipSuccess) return e;
+    s.pending = false;
+  }
+  if (!s.ev) {
+    e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+  }
+  if (s.cap < bytes) {
+    if (s.host) (void)hipHostFree(s.host);
+    s.host = nullptr;
+    s.cap = 0;
+    const size_t cap = std::max<size_t>(align_up(bytes, 65536), 65536);
+    e = hipHostMalloc(&s.host, cap, hipHostMallocPortable);
+    if (e != hipSuccess) return e;
+    s.cap = cap;
+  }
+  std::memcpy(s.host, src, bytes);
+  e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(s.ev, stream);
+  if (e != hipSuccess) return e;
+  s.pending = true;
+  return hipSuccess;
+}
+
+hipError_t upload_args(void* dst, const void* src, size_t bytes, hipStream_t stream) {
   const unsigned char* from = static_cast<const unsigned char*>(src);
   unsigned char* to = static_cast<unsigned char*>(dst);
   TableChunk chunk;
@@ -81,6 +136,19 @@ hipError_t upload(void* dst, const void* src, size_t bytes, hipStream_t stream) 
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// The copy path unless the stream is capturing (or its status is unknown)
+// or the caller must not allocate.
+hipError_t upload(void* dst, const void* src, size_t bytes, hipStream_t stream,
+                  bool may_allocate = true) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    cs = hipStreamCaptureStatusActive;
+  }
+  if (may_allocate && cs == hipStreamCaptureStatusNone) return upload_copy(dst, src, bytes, stream);
+  return upload_args(dst, src, bytes, stream);
 }
 
 // ----------------------------------------------------------------- checks
@@ -136,6 +204,7 @@ struct Stage {
   size_t off;   // byte offset of its descriptors inside the table
   int count;    // descriptors
   int total;    // workgroups (chunks / tiles)
+  bool small = false;   // GEMM on 64 x 64 tiles
   double work;  // algorithmic flops (GEMM) or HBM bytes (normalisation)
 };
 
@@ -256,6 +325,8 @@ void layout(Plan& pl, const ns_matrix* mats, int count, ns_backend be, int shard
   });
 }
 
+void set_tiles(GemmDesc& d, int T);
+
 struct Builder {
   Plan& pl;
   unsigned char* ws;   // device base (may be null while sizing)
@@ -278,19 +349,26 @@ struct Builder {
   }
 
   // One grouped GEMM launch; problems ordered by tile cost (K), largest
-  // first, so long tiles start early and short ones fill the tail.
-  void gemm_stage(Probs pr) {
+  // first, so long tiles start early and short ones fill the tail. A stage
+  // with fewer than SMALL_STAGE_TILES 256-tiles (too few to occupy the
+  // chip) runs on 64 x 64 tiles instead; both kernels give the same bits.
+  void gemm_stage(Probs pr, int force_edge = 0) {
     std::vector<GemmDesc>& v = pr.d;
     std::stable_sort(v.begin(), v.end(), [](const GemmDesc& a, const GemmDesc& b) {
       if (a.K != b.K) return a.K > b.K;
       return a.tiles > b.tiles;
     });
+    int big = 0;
+    for (auto& d : v) big += d.tiles;
+    const bool small = force_edge ? force_edge == gemm_small_tile() : big < SMALL_STAGE_TILES;
     int begin = 0;
     for (auto& d : v) {
+      if (small) set_tiles(d, gemm_small_tile());
       d.tile_begin = begin;
       begin += d.tiles;
     }
     push(Stage::GEMM, v, begin, pr.flops);
+    if (!v.empty()) pl.stages.back().small = small;
   }
 
   // One launch of shard reductions (HBM-bound: every part read once, the
@@ -308,6 +386,19 @@ struct Builder {
   }
 };
 
+// Tile counts of a descriptor for tiles of edge T: the lower triangle of
+// the tile grid for a symmetric problem, the whole grid otherwise.
+void set_tiles(GemmDesc& d, int T) {
+  if (d.symmetric) {
+    const int t = d.M / T;
+    d.tiles_n = t;
+    d.tiles = t * (t + 1) / 2;
+  } else {
+    d.tiles_n = d.N / T;
+    d.tiles = (d.M / T) * (d.N / T);
+  }
+}
+
 GemmDesc gemm(const _Float16* A, const _Float16* B, const _Float16* C, void* D,
               _Float16* D2, _Float16* DT, int64_t M, int64_t N, int64_t K, int64_t ldd,
               int64_t valid_m, int64_t valid_n, int64_t diag_n, int out_type, bool sym,
@@ -323,14 +414,7 @@ GemmDesc gemm(const _Float16* A, const _Float16* B, const _Float16* C, void* D,
   d.diag_n = static_cast<int>(diag_n);
   d.out_type = out_type;
   d.symmetric = sym ? 1 : 0;
-  if (sym) {
-    const int t = static_cast<int>(M / T);
-    d.tiles_n = t;
-    d.tiles = t * (t + 1) / 2;
-  } else {
-    d.tiles_n = static_cast<int>(N / T);
-    d.tiles = static_cast<int>((M / T) * (N / T));
-  }
+  set_tiles(d, T);
   d.alpha = alpha; d.beta = beta; d.gamma = gamma; d.delta = delta;
   return d;
 }
@@ -724,9 +808,9 @@ EpiKind epilogue_kind(const GemmDesc& d) {
   return EK_GENERAL;
 }
 
-bool check_gemm(const GemmDesc& d, Bounds& B) {
-  const int T = gemm_tile();
-  if (d.M <= 0 || d.N <= 0 || d.K <= 0 || d.M % T || d.N % T || d.K % gemm_k_multiple())
+bool check_gemm(const GemmDesc& d, Bounds& B, int T) {
+  if (d.M <= 0 || d.N <= 0 || d.K <= 0 || d.M % gemm_tile() || d.N % gemm_tile() ||
+      d.K % gemm_k_multiple())
     return B.fail("gemm: M, N or K is not a multiple of the tile");
   if (d.symmetric && d.M != d.N) return B.fail("gemm: symmetric product that is not square");
   const int tm = d.M / T, tn = d.N / T;
@@ -781,7 +865,7 @@ bool validate_plan(const Plan& pl, const unsigned char* ws, Bounds& B) {
         for (int i = 0; i < st.count; ++i) {
           if (d[i].tile_begin != next) return B.fail("gemm: tile ranges not contiguous");
           next += d[i].tiles;
-          if (!check_gemm(d[i], B)) return false;
+          if (!check_gemm(d[i], B, st.small ? gemm_small_tile() : gemm_tile())) return false;
         }
         if (next != st.total) return B.fail("gemm: launch size differs from its tiles");
         break;
@@ -989,11 +1073,13 @@ hipError_t timed(bool on, bool gemm_kind, double work, hipStream_t stream, F lau
   return e;
 }
 
+// may_allocate == false: no pinned staging memory and no timing events.
 ns_status run_plan(const Plan& pl, unsigned char* ws, hipStream_t stream,
-                   bool allow_timing = true) {
+                   bool may_allocate = true) {
   unsigned char* table = ws + pl.table_off;
-  if (upload(table, pl.table.data(), pl.table.size(), stream) != hipSuccess) return NS_ERR_HIP;
-  const bool on = allow_timing && timing_on();
+  if (upload(table, pl.table.data(), pl.table.size(), stream, may_allocate) != hipSuccess)
+    return NS_ERR_HIP;
+  const bool on = may_allocate && timing_on();
   for (const Stage& st : pl.stages) {
     hipError_t e = hipSuccess;
     switch (st.kind) {
@@ -1017,8 +1103,9 @@ ns_status run_plan(const Plan& pl, unsigned char* ws, hipStream_t stream,
         break;
       case Stage::GEMM:
         e = timed(on, true, st.work, stream, [&] {
-          return launch_gemm(reinterpret_cast<const GemmDesc*>(table + st.off), st.count,
-                             st.total, stream);
+          const GemmDesc* d = reinterpret_cast<const GemmDesc*>(table + st.off);
+          return st.small ? launch_gemm_small(d, st.count, st.total, stream)
+                          : launch_gemm(d, st.count, st.total, stream);
         });
         break;
       case Stage::REDUCE:
@@ -1055,7 +1142,7 @@ ns_status check_shards(const ns_matrix& a, int shards) {
 ns_status run_batched(const ns_matrix* mats, int count, ns_backend be, const ns_params* p,
                       void* ws, size_t ws_bytes, void* stream, int shards = 1,
                       const ns_muon_matrix* muon = nullptr, float beta = 0.f, float lr = 0.f,
-                      bool allow_timing = true) {
+                      bool may_allocate = true) {
   ns_status s = check_call(mats, count, be, p);
   if (s != NS_OK) return s;
   if (count == 0) return NS_OK;
@@ -1071,7 +1158,7 @@ ns_status run_batched(const ns_matrix* mats, int count, ns_backend be, const ns_
   Bounds bounds;
   allow_buffers(bounds, pl, w, mats, count);
   if (!validate_plan(pl, w, bounds)) return NS_ERR_INTERNAL;
-  return run_plan(pl, w, static_cast<hipStream_t>(stream), allow_timing);
+  return run_plan(pl, w, static_cast<hipStream_t>(stream), may_allocate);
 }
 
 std::string g_info;
@@ -1465,9 +1552,11 @@ NS_API ns_status ns_gemm_grouped_workspace_size(int count, size_t* bytes) {
   return NS_OK;
 }
 
-NS_API ns_status ns_gemm_grouped(const ns_gemm_problem* probs, int count, void* ws,
-                                 size_t ws_bytes, void* stream) {
+NS_API ns_status ns_gemm_grouped(const ns_gemm_problem* probs, int count, int tile_edge,
+                                 void* ws, size_t ws_bytes, void* stream) {
   if (count < 0 || (count > 0 && !probs)) return NS_ERR_INVALID_ARG;
+  if (tile_edge != 0 && tile_edge != gemm_tile() && tile_edge != gemm_small_tile())
+    return NS_ERR_INVALID_ARG;
   if (count == 0) return NS_OK;
   Probs v;
   for (int i = 0; i < count; ++i) {
@@ -1486,14 +1575,20 @@ NS_API ns_status ns_gemm_grouped(const ns_gemm_problem* probs, int count, void* 
     if (a.K != b.K) return a.K > b.K;
     return a.tiles > b.tiles;
   });
+  int big = 0;
+  for (auto& d : v.d) big += d.tiles;
+  const bool small = tile_edge ? tile_edge == gemm_small_tile() : big < SMALL_STAGE_TILES;
   int begin = 0;
   for (auto& d : v.d) {
+    if (small) set_tiles(d, gemm_small_tile());
     d.tile_begin = begin;
     begin += d.tiles;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (upload(ws, v.d.data(), v.d.size() * sizeof(GemmDesc), st) != hipSuccess) return NS_ERR_HIP;
-  if (launch_gemm(static_cast<const GemmDesc*>(ws), count, begin, st) != hipSuccess)
+  const GemmDesc* dd = static_cast<const GemmDesc*>(ws);
+  if ((small ? launch_gemm_small(dd, count, begin, st) : launch_gemm(dd, count, begin, st)) !=
+      hipSuccess)
     return NS_ERR_HIP;
   return NS_OK;
 }
@@ -1595,5 +1690,5 @@ NS_API ns_status ns_batched_noalloc(const ns_matrix* mats, int count, ns_backend
   s = scratch_address(&ws);
   if (s != NS_OK) return s;
   return run_batched(mats, count, backend, params, ws, NS_NOALLOC_SCRATCH_BYTES, stream, 1,
-                     nullptr, 0.f, 0.f, /*allow_timing=*/false);
+                     nullptr, 0.f, 0.f, /*may_allocate=*/false);
 }

@@ -146,6 +146,12 @@ hipError_t launch_cast(const NormDesc* descs, int count, int total_tiles,
                        hipStream_t stream);
 hipError_t launch_gemm(const GemmDesc* descs, int count, int total_tiles,
                        hipStream_t stream);
+// The same products on 64 x 64 tiles (tile counts and tile_begin of the
+// descriptors in units of 64 x 64 tiles, symmetric problems as the rows of
+// their lower triangle); bitwise the same results as launch_gemm.
+hipError_t launch_gemm_small(const GemmDesc* descs, int count, int total_tiles,
+                             hipStream_t stream);
+int gemm_small_tile();
 hipError_t launch_reduce(const ReduceDesc* descs, int count, int total_blocks,
                          hipStream_t stream);
 

@@ -236,3 +236,65 @@ def test_clipped_caller_buffers(d_dtype, c_dtype):
     X64 = to64(X)
     assert_bound(to64(from_pairs(R)), X64 @ X64.T, acc_bound(1024, 1.0, X64, X64),
                  torch.float16, "syrk 4096x1024")
+
+
+def _path_problems(seed):
+    """One problem per epilogue path, at sizes both kernels tile: symmetric
+    with fold and D2, symmetric with C read in the epilogue, SYRK, full with
+    fold and the transposed output, and clipped caller buffers of each type
+    combination."""
+    S = sym16(512, seed)
+    T = sym16(512, seed + 1)
+    X = rand16((512, 1024), 1.0 / 32, seed + 2)
+    Q = rand16((512, 512), 1.0 / 22, seed + 3)
+    A = rand16((512, 384), 1.0 / 20, seed + 4)
+    Bm = rand16((768, 384), 1.0, seed + 5)
+    C32 = torch.randn((300, 701), device="cuda")
+    Cbf = torch.randn((300, 701), device="cuda").to(torch.bfloat16)
+    Sp, Tp, Xp = to_pairs(S), to_pairs(T), to_pairs(X)
+
+    def outs():
+        e = lambda *sh, dt=torch.float16: torch.full(sh, 5.0, dtype=dt, device="cuda")
+        return dict(z=e(512, 512), q=e(512, 512), r=e(512, 512), syrk=e(512, 512),
+                    x=e(512, 1024), xt=e(1024, 512), cl1=e(300, 703, dt=torch.bfloat16),
+                    cl2=e(300, 703, dt=torch.float32), cl3=e(300, 703))
+    def probs(o):
+        return [
+            dict(a=Sp, b=Sp, c=Sp, d=o["z"], d2=o["q"], M=512, N=512, K=512, symmetric=1,
+                 c_is_bt=1, a_pairs=1, b_pairs=1, c_pairs=1, d_pairs=1, alpha=0.47, beta=-2.5,
+                 delta=3.9, diag_n=500),
+            dict(a=Tp, b=Sp, c=Tp, d=o["r"], M=512, N=512, K=512, symmetric=1, a_pairs=1,
+                 b_pairs=1, c_pairs=1, d_pairs=1, alpha=1.0, beta=2.19, gamma=0.5,
+                 diag_n=511),
+            dict(a=Xp, b=Xp, d=o["syrk"], M=512, N=512, K=1024, symmetric=1, a_pairs=1,
+                 b_pairs=1, d_pairs=1),
+            dict(a=to_pairs(Q), b=to_pairs(X.T.contiguous()), c=Xp, d=o["x"], dt=o["xt"],
+                 M=512, N=1024, K=512, c_is_bt=1, a_pairs=1, b_pairs=1, c_pairs=1, d_pairs=1,
+                 alpha=1.0, beta=2.87),
+            dict(a=A, b=Bm, c=C32, d=o["cl1"], M=512, N=768, K=384, ldc=701, ldd=703,
+                 valid_m=300, valid_n=700, diag_n=300, alpha=0.7, beta=-1.3, gamma=0.25),
+            dict(a=A, b=Bm, c=Cbf, d=o["cl2"], M=512, N=768, K=384, ldc=701, ldd=703,
+                 valid_m=300, valid_n=700, diag_n=300, alpha=-0.02, beta=1.0),
+            dict(a=A, b=Bm, d=o["cl3"], M=512, N=768, K=384, ldd=703, valid_m=300,
+                 valid_n=700, diag_n=0, alpha=1.0),
+        ]
+    return outs, probs
+
+
+@pytest.mark.parametrize("seed", [21, 22])
+def test_small_tile_kernel_gives_the_same_bits(seed):
+    """The 64 x 64 tile kernel (used for stages with few 256-tiles, e.g. a
+    single small matrix) against the 256 x 256 tile kernel on every epilogue
+    path: the same MFMA over the same k steps, the same fold point and the
+    same epilogue arithmetic, so every output must be bitwise equal, and
+    untouched where neither may write."""
+    require_gpu()
+    outs, probs = _path_problems(seed)
+    big, small = outs(), outs()
+    nsmi.ns_gemm_grouped(probs(big), tile_edge=256)
+    nsmi.ns_gemm_grouped(probs(small), tile_edge=64)
+    torch.cuda.synchronize()
+    for k in big:
+        assert torch.equal(big[k], small[k]), k
+    for k in ("cl1", "cl2", "cl3"):
+        assert torch.all(big[k][:, 700:].float() == 5.0), k
