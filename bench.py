@@ -458,8 +458,9 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "target": target_status(tflops, n, w, ms, len(table)),
-        "config": {"workload": f"Llama-3-8B owner share: 28 projections (4 x q/k/v/o/gate/up/"
-                               f"down), bf16 N(0,1) gradients, one ns_batched call",
+        "config": {"workload": (f"Llama-3-8B owner share: 28 projections (4 x q/k/v/o/gate/"
+                                f"up/down), bf16 N(0,1) gradients, one ns_batched call"
+                                if args.workload == 4 else f"{w.name}, one ns_batched call"),
                    "matrices": n, "backend": args.backend, "coefficients": w.coefficients,
                    "restarts": list(restarts), "eps": 1e-7, "input_dtype": w.dtype,
                    "output_dtype": "f16"},
