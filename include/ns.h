@@ -291,7 +291,13 @@ ns_status ns_gemm_nt(const void* a, const void* b, const void* c, void* d,
  *   d[i][j]  = v                                (type d_dtype, leading dim ldd)
  *   d2[i][j] = v + (i == j < diag_n ? delta : 0)           (fp16, leading dim N)
  *   dt[j][i] = v                                 (fp16, leading dim M)
- *   a (M, K) and b (N, K): fp16, leading dimension K;
+ *   a (M, K) and b (N, K): fp16, leading dimension K; or, with a_kmajor
+ *             (b_kmajor), a stored as its (K, M) transpose with leading
+ *             dimension M (b as (K, N), leading dimension N), which needs
+ *             the row-pair layout (a_pairs / b_pairs = 1); at most one
+ *             operand K-major, not in the symmetric mode, and not b with
+ *             c_is_bt. This is how the Gram iteration multiplies by X
+ *             without a transposed copy of it;
  *   c (M, N): type c_dtype, leading dimension ldc, or NULL (then beta is
  *             not used);
  *   *_pairs:  1 = the row-pair layout the iteration keeps its fp16 buffers
@@ -328,6 +334,7 @@ typedef struct {
   ns_dtype c_dtype, d_dtype;
   int symmetric, c_is_bt;
   int a_pairs, b_pairs, c_pairs, d_pairs;
+  int a_kmajor, b_kmajor;
   float alpha, beta, gamma, delta;
 } ns_gemm_problem;
 ns_status ns_gemm_grouped_workspace_size(int count, size_t* bytes);

@@ -104,6 +104,7 @@ class _GemmProblem(ctypes.Structure):
                 ("symmetric", ctypes.c_int), ("c_is_bt", ctypes.c_int),
                 ("a_pairs", ctypes.c_int), ("b_pairs", ctypes.c_int),
                 ("c_pairs", ctypes.c_int), ("d_pairs", ctypes.c_int),
+                ("a_kmajor", ctypes.c_int), ("b_kmajor", ctypes.c_int),
                 ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
                 ("gamma", ctypes.c_float), ("delta", ctypes.c_float)]
 
@@ -532,12 +533,14 @@ def ns_gemm_grouped(problems: List[dict], tile_edge: int = 0) -> None:
     one launch (kernel-level testing; see ns_gemm_problem in ns.h).
 
     Each problem is a dict: "a", "b", "d" (GPU tensors; a and b fp16 holding
-    M*K and N*K elements in the layout their *_pairs flag names), optional
-    "c", "d2", "dt", the sizes "M", "N", "K", and optionally "ldc", "ldd"
-    (default N), "valid_m", "valid_n" (default M, N), "diag_n" (default 0),
-    "symmetric", "c_is_bt", "a_pairs", "b_pairs", "c_pairs", "d_pairs"
-    (default 0), "alpha" (1), "beta", "gamma", "delta" (0). tile_edge: 256
-    or 64 forces that kernel, 0 picks as the iteration's stages do."""
+    M*K and N*K elements in the layout their *_pairs flag names, a as
+    (K, M) and b as (K, N) if "a_kmajor" / "b_kmajor"), optional "c", "d2",
+    "dt", the sizes "M", "N", "K", and optionally "ldc", "ldd" (default N),
+    "valid_m", "valid_n" (default M, N), "diag_n" (default 0), "symmetric",
+    "c_is_bt", "a_pairs", "b_pairs", "c_pairs", "d_pairs", "a_kmajor",
+    "b_kmajor" (default 0), "alpha" (1), "beta", "gamma", "delta" (0).
+    tile_edge: 256 or 64 forces that kernel, 0 picks as the iteration's
+    stages do."""
     if not problems:
         return
     arr = (_GemmProblem * len(problems))()
@@ -559,6 +562,7 @@ def ns_gemm_grouped(problems: List[dict], tile_edge: int = 0) -> None:
             int(q.get("symmetric", 0)), int(q.get("c_is_bt", 0)),
             int(q.get("a_pairs", 0)), int(q.get("b_pairs", 0)),
             int(q.get("c_pairs", 0)), int(q.get("d_pairs", 0)),
+            int(q.get("a_kmajor", 0)), int(q.get("b_kmajor", 0)),
             float(q.get("alpha", 1.0)), float(q.get("beta", 0.0)),
             float(q.get("gamma", 0.0)), float(q.get("delta", 0.0)))
     lib = library()

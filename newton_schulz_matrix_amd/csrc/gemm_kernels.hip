@@ -8,8 +8,8 @@
 //
 // because every Gram-space matrix (R, Z, T, Q) is symmetric in exact
 // arithmetic and is stored exactly symmetric (lower-triangle tiles computed,
-// then mirrored), so a symmetric right operand B equals B^T; and the
-// iteration keeps X^T next to X so that Q X = Q (X^T)^T is NT as well.
+// then mirrored), so a symmetric right operand B equals B^T; and Q X reads
+// X as a K-major right operand (the direct-space step keeps X^T instead).
 //
 // Uses on the "Newton-Schulz 变体" page: the Gram product R = X X^T
 // (section "Gram 空间 NS", SYRK: lower-triangle tiles only, about half the
@@ -38,6 +38,10 @@
 //     (16 consecutive rows) hit 16 distinct bank groups;
 //   * workgroup ids are remapped so each XCD (8 per MI355X, one L2 each)
 //     works on runs of 32 neighbouring tiles that share operand panels;
+//   * either operand may instead be K-major (stored K x width in the
+//     row-pair layout, see km_off): X serves as the right operand of Q X,
+//     or as the left one of X^T Q, without a transposed copy; its slices
+//     are copied by pairs of k rows and read with transposing LDS reads;
 //   * on a diagonal tile of a symmetric product group 0's four waves split
 //     the 128 stored columns of their rows (32 each) rather than two of them
 //     computing the never-stored upper-right quadrant;
@@ -359,6 +363,51 @@ __device__ __forceinline__ u32x2 lds_read_tr(const lds_char* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// K-major operand slices. A K-major operand is stored as (K x width) in the
+// row-pair layout, so one pair of k rows over a tile's columns is a single
+// contiguous run of whole 128-byte lines (32 columns of both rows each); a
+// K slice of 32 is 16 such pairs, one copy instruction per pair (1 KB for
+// 256 columns). In LDS, pair q of a slice takes PAIR halves: the 64-half
+// unit of column block c (both rows, 32 columns each) sits at unit
+// c ^ (q & 1), and the two 16-column halves of each row are swapped when
+// bit 2 of q is set. A fragment is then read with two transposing reads,
+// each giving a lane four consecutive k of one column; the 32 lanes of a
+// half wave touch two pairs at opposite unit parity and the lanes 8 k
+// apart touch the other halves of the rows, so the reads spread over all
+// bank groups.
+template <int PAIR>
+__device__ __forceinline__ int km_off(int q, int r, int c, int w) {
+  return q * PAIR + ((c ^ (q & 1)) << 6) + (r << 5) + (w ^ (((q >> 2) & 1) << 4));
+}
+
+// Offset (halves) from a slice's first pair at the tile's first column of
+// the 16 bytes that copy slot s (0..7) of unit u of pair q must fetch so
+// that they land where km_off reads them (width = leading dimension).
+__device__ __forceinline__ int64_t km_src(int q, int u, int s, int64_t width) {
+  const int c = u ^ (q & 1);
+  const int w = ((s & 3) * 8) ^ (((q >> 2) & 1) << 4);
+  return static_cast<int64_t>(q) * 2 * width + c * 64 + (s >> 2) * 32 + w;
+}
+
+// MFMA operand fragment of 32 operand rows (slice columns col .. col + 31)
+// at k step ks from a K-major slice: lane l receives k 16 ks + 8 (l / 32)
+// + 0..7 of column col + l % 32, as a row-major slice's 16-byte read gives.
+// A 16-lane group covers 16 columns and four k per transposing read: its
+// lane j points at k row kb + j / 4, columns 4 (j % 4) .. + 3.
+template <int PAIR>
+__device__ __forceinline__ half8 km_frag(const _Float16* S, int col, int ks, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int n = col + 16 * (g & 1) + 4 * (j & 3);
+  const int c = n >> 5, w = n & 31;
+  const lds_char* const Sl = (const lds_char*)(S);
+  const int k0 = 16 * ks + 8 * (g >> 1) + (j >> 2);
+  const int k1 = k0 + 4;
+  const u32x2 v0 = lds_read_tr(Sl + 2 * km_off<PAIR>(k0 >> 1, k0 & 1, c, w));
+  const u32x2 v1 = lds_read_tr(Sl + 2 * km_off<PAIR>(k1 >> 1, k1 & 1, c, w));
+  const u32x4 x = {v0[0], v0[1], v1[0], v1[1]};
+  return __builtin_bit_cast(half8, x);
+}
+
 enum EpiMode { EPI_SYM_OFFDIAG, EPI_SYM_DIAG, EPI_FULL, EPI_FULL_C };
 
 // Fast epilogue for fp16 outputs inside internal (padded, aligned) buffers:
@@ -545,7 +594,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   // m0 / BK + wm * FM + I. With WM == STAGES * BK that slice sits in ring
   // position I of ring round m0 / (STAGES * BK) + wm.
   static_assert(C::FM == STAGES && C::WM == STAGES * C::BK, "fold: one ring round per wave");
-  const bool fold = d.c_is_bt != 0;
+  const bool fold = d.c_is_bt != 0 && !d.b_kmajor;   // the fold reads row-major B slices
   const float rho = fold ? d.beta / d.alpha : 0.f;
   const int fold_round = fold ? m0 / (STAGES * C::BK) + wm : -1;
 
@@ -564,45 +613,78 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   // Offsets are relative to the tile's row panel; the K position goes in
   // the scalar offset: 2 bytes per column of a row-major operand, 4 in the
   // row-pair layout (a 32-column block of two rows is 128 bytes).
+  // A K-major operand is copied by pairs of k rows instead (km_src): copy i
+  // of wave gw fetches pair 4 gw + i of the slice, and the buffer
+  // descriptor is rebased on every slice (the K offset k0 * width may
+  // exceed 32 bits).
   constexpr int RPB = 1024 / (C::BK * 2);          // rows per copy instruction
   constexpr int COPIES = C::BM / RPB / C::WAVES_N; // per wave and slice
   static_assert(C::WAVES_M == 2 && COPIES == 4, "ping-pong plan: two groups of four waves");
+  static_assert(C::A_ELEMS == 16 * 2 * C::BM, "K-major slice: 16 pairs of k rows per slice");
   const int grp = wm, gw = wn;
   const bool my_pairs = (grp == 0 ? d.a_pairs : d.b_pairs) != 0;
+  const bool my_km = (grp == 0 ? d.a_kmajor : d.b_kmajor) != 0;
+  const int64_t my_width = grp == 0 ? M : N;        // leading dimension if K-major
+  const _Float16* const my_km_base = grp == 0 ? d.A + 2 * static_cast<int64_t>(m0)
+                                              : d.B + 2 * static_cast<int64_t>(n0);
   const uint32_t panel_bytes = static_cast<uint32_t>(C::BM) * K * 2u;
   const i32x4 rMy = grp == 0 ? make_rsrc(d.A + static_cast<int64_t>(m0) * K, panel_bytes)
                              : make_rsrc(d.B + static_cast<int64_t>(n0) * K, panel_bytes);
   const uint32_t kbytes = my_pairs ? 4u : 2u;
   uint32_t my_off[COPIES];
   static_for<0, COPIES>([&](auto i) {
-    const int row = (gw * COPIES + i) * RPB + lane / C::KCH;
-    const int col = ((lane % C::KCH) ^ swz(row)) * 8;
-    my_off[i] = static_cast<uint32_t>(my_pairs ? (row >> 1) * 2 * K + (row & 1) * 32 + col
-                                               : row * K + col) * 2u;
+    if (my_km) {
+      my_off[i] = static_cast<uint32_t>(km_src(gw * COPIES + i, lane >> 3, lane & 7, my_width)) * 2u;
+    } else {
+      const int row = (gw * COPIES + i) * RPB + lane / C::KCH;
+      const int col = ((lane % C::KCH) ^ swz(row)) * 8;
+      my_off[i] = static_cast<uint32_t>(my_pairs ? (row >> 1) * 2 * K + (row & 1) * 32 + col
+                                                 : row * K + col) * 2u;
+    }
   });
   // this wave's share of slice k0 of its group's operand into ring stage s
-  auto copy_my = [&](int s, int k0) {
-    const uint32_t kb = static_cast<uint32_t>(k0) * kbytes;
+  // (KM: the operand is K-major)
+  auto copy_my = [&](int s, int k0, auto KM) {
     _Float16* base = (grp == 0 ? stA(s) : stB(s)) + gw * COPIES * 512;
-    static_for<0, COPIES>([&](auto i) {
-      lds_copy16(rMy, lds_addr_of(base + i * 512), my_off[i], kb);
-    });
+    if constexpr (decltype(KM)::value) {
+      const i32x4 r = make_rsrc(my_km_base + static_cast<int64_t>(k0) * my_width,
+                                static_cast<uint32_t>(32 * my_width * 2));
+      static_for<0, COPIES>([&](auto i) {
+        lds_copy16(r, lds_addr_of(base + i * 512), my_off[i], 0u);
+      });
+    } else {
+      const uint32_t kb = static_cast<uint32_t>(k0) * kbytes;
+      static_for<0, COPIES>([&](auto i) {
+        lds_copy16(rMy, lds_addr_of(base + i * 512), my_off[i], kb);
+      });
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
   // One fragment register set per wave: a wave reads the next slice's
   // fragments only in the phase after issuing its MFMAs of the current one.
   half8 fa0[C::KSTEPS][C::FM], fb0[C::KSTEPS][C::FN];
-  auto read_frags = [&](const _Float16* SA, const _Float16* SB, auto& fa, auto& fb) {
+  constexpr int KM_PAIR = 2 * C::BM;   // halves per pair of k rows in a K-major slice
+  auto read_frags = [&](const _Float16* SA, const _Float16* SB, auto& fa, auto& fb, auto AK,
+                        auto BK) {
     static_for<0, C::KSTEPS>([&](auto KS) {
       const int kc = KS * 2 + (lane >> 5);
       static_for<0, C::FM>([&](auto I) {
-        const int row = wm * C::WM + I * 32 + (lane & 31);
-        fa[KS][I] = *reinterpret_cast<const half8*>(&SA[row * C::BK + ((kc ^ swz(row)) * 8)]);
+        if constexpr (decltype(AK)::value) {
+          fa[KS][I] = km_frag<KM_PAIR>(SA, wm * C::WM + I * 32, KS, lane);
+        } else {
+          const int row = wm * C::WM + I * 32 + (lane & 31);
+          fa[KS][I] = *reinterpret_cast<const half8*>(&SA[row * C::BK + ((kc ^ swz(row)) * 8)]);
+        }
       });
       static_for<0, C::FN>([&](auto J) {
         if (J == 0 || !half_cols) {
-          const int row = bcol0 + J * 32 + (lane & 31);
-          fb[KS][J] = *reinterpret_cast<const half8*>(&SB[row * C::BK + ((kc ^ swz(row)) * 8)]);
+          if constexpr (decltype(BK)::value) {
+            fb[KS][J] = km_frag<KM_PAIR>(SB, bcol0 + J * 32, KS, lane);
+          } else {
+            const int row = bcol0 + J * 32 + (lane & 31);
+            fb[KS][J] =
+                *reinterpret_cast<const half8*>(&SB[row * C::BK + ((kc ^ swz(row)) * 8)]);
+          }
         }
       });
     });
@@ -671,14 +753,19 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   // last slice into a stage that is never consumed again.
   const int nk = K / C::BK;
   auto kclamp = [&](int sl) { return min(sl, nk - 1) * C::BK; };
-  auto k_loop = [&](auto HALF) {
-  static_for<0, STAGES>([&](auto s) { copy_my(s, kclamp(s)); });
+  // HALF as above; AK / BK: A / B is K-major (at most one; never with HALF).
+  // The fold is compiled only where B slices are row-major.
+  auto k_loop = [&](auto HALF, auto AK, auto BK) {
+  constexpr bool FOLD_OK = !decltype(BK)::value;
+  if (grp == 0) static_for<0, STAGES>([&](auto s) { copy_my(s, kclamp(s), AK); });
+  else static_for<0, STAGES>([&](auto s) { copy_my(s, kclamp(s), BK); });
   // only slice 0 is read before the next wait; slices 1-3 keep streaming
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * COPIES) & ~0x0F00);
   __builtin_amdgcn_s_barrier();
   if (grp == 0) {
-    read_frags(stA(0), stB(0), fa0, fb0);
-    if (fold_round == 0) fold_c(stB(0), std::integral_constant<int, 0>{});
+    read_frags(stA(0), stB(0), fa0, fb0, AK, BK);
+    if constexpr (FOLD_OK)
+      if (fold_round == 0) fold_c(stB(0), std::integral_constant<int, 0>{});
     phase_end();
     for (int kt = 0; kt < nk; kt += STAGES) {
       static_for<0, STAGES>([&](auto U) {
@@ -689,10 +776,11 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
         auto& fbn = fb0;
         mfma_phase(fa, fb, HALF);
         phase_end();
-        copy_my(u, kclamp(kt + u + 4));
-        read_frags(stA((u + 1) % STAGES), stB((u + 1) % STAGES), fan, fbn);
-        if (kt / STAGES + (u == STAGES - 1 ? 1 : 0) == fold_round)
-          fold_c(stB((u + 1) % STAGES), std::integral_constant<int, (u + 1) % STAGES>{});
+        copy_my(u, kclamp(kt + u + 4), AK);
+        read_frags(stA((u + 1) % STAGES), stB((u + 1) % STAGES), fan, fbn, AK, BK);
+        if constexpr (FOLD_OK)
+          if (kt / STAGES + (u == STAGES - 1 ? 1 : 0) == fold_round)
+            fold_c(stB((u + 1) % STAGES), std::integral_constant<int, (u + 1) % STAGES>{});
         phase_end();
       });
     }
@@ -703,9 +791,10 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
         constexpr int u = U;
         auto& fa = fa0;
         auto& fb = fb0;
-        if (kt + u >= 1) copy_my((u + 3) % STAGES, kclamp(kt + u + 3));
-        read_frags(stA(u), stB(u), fa, fb);
-        if (kt / STAGES == fold_round) fold_c(stB(u), std::integral_constant<int, u>{});
+        if (kt + u >= 1) copy_my((u + 3) % STAGES, kclamp(kt + u + 3), BK);
+        read_frags(stA(u), stB(u), fa, fb, AK, BK);
+        if constexpr (FOLD_OK)
+          if (kt / STAGES == fold_round) fold_c(stB(u), std::integral_constant<int, u>{});
         phase_end();
         mfma_phase(fa, fb, HALF);
         phase_end();
@@ -713,8 +802,10 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
     }
   }
   };
-  if (half_cols) k_loop(std::true_type{});
-  else k_loop(std::false_type{});
+  if (half_cols) k_loop(std::true_type{}, std::false_type{}, std::false_type{});
+  else if (d.a_kmajor) k_loop(std::false_type{}, std::true_type{}, std::false_type{});
+  else if (d.b_kmajor) k_loop(std::false_type{}, std::false_type{}, std::true_type{});
+  else k_loop(std::false_type{}, std::false_type{}, std::false_type{});
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));   // trailing copies
   __builtin_amdgcn_s_barrier();
 
@@ -759,6 +850,9 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
 // CU per stage). Four waves, each owning one 32 x 32 block of
 // v_mfma_f32_32x32x16_f16; a four-stage ring of 64 x 32 operand slices
 // filled by the same buffer-to-LDS copies; per-element epilogue.
+//
+// K-major operands as in gemm_nt_kernel, with 64-column pairs of k rows
+// (256 bytes each; one copy instruction moves four of them).
 //
 // Every output element is produced exactly as gemm_nt_kernel produces it:
 // the same MFMA over the same 16-wide k steps in the same order, beta * C
@@ -836,6 +930,10 @@ __device__ __forceinline__ void small_epilogue(const floatx16& acc, const GemmDe
   }
 }
 
+// KM: the launch may hold K-major operands. Stages without them use the
+// KM = false kernel, whose code is a third the size: this kernel's stages
+// are short, and each workgroup starts on a cold instruction cache.
+template <bool KM>
 __global__ __launch_bounds__(SM_THREADS) void gemm_small_kernel(
     const GemmDesc* __restrict__ descs, int count, int total_tiles) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -858,65 +956,98 @@ __global__ __launch_bounds__(SM_THREADS) void gemm_small_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const bool fold = d.c_is_bt != 0;
+  const bool fold = d.c_is_bt != 0 && !d.b_kmajor;
   const float rho = fold ? d.beta / d.alpha : 0.f;
   const int fold_slice = (m0 + 32 * wm) / SM_BK;   // this wave's rows arrive with this K slice
   floatx16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
-  // copies: wave w fills rows 16 w .. 16 w + 15 of the A and of the B slice
+  // copies: wave w fills rows 16 w .. 16 w + 15 of the A and of the B slice,
+  // or, for a K-major operand, pairs of k rows 4 w .. 4 w + 3 (km_src; the
+  // descriptor rebased on every slice as in gemm_nt_kernel). AK / BK: A / B
+  // is K-major, chosen once per tile so the loop has no per-slice branches.
   const uint32_t panel = static_cast<uint32_t>(SM_TILE) * K * 2u;
-  const i32x4 rA = make_rsrc(d.A + static_cast<int64_t>(m0) * K, panel);
-  const i32x4 rB = make_rsrc(d.B + static_cast<int64_t>(n0) * K, panel);
-  const int row = wave * 16 + lane / 4;
-  const int col = ((lane % 4) ^ swz(row)) * 8;
-  const uint32_t offA = static_cast<uint32_t>(d.a_pairs ? (row >> 1) * 2 * K + (row & 1) * 32 + col
-                                                        : row * K + col) * 2u;
-  const uint32_t offB = static_cast<uint32_t>(d.b_pairs ? (row >> 1) * 2 * K + (row & 1) * 32 + col
-                                                        : row * K + col) * 2u;
-  const uint32_t kbA = d.a_pairs ? 4u : 2u, kbB = d.b_pairs ? 4u : 2u;
   const int nk = K / SM_BK;
-  auto copy_slice = [&](int s, int sl) {
-    const uint32_t k0 = static_cast<uint32_t>(min(sl, nk - 1) * SM_BK);
-    lds_copy16(rA, lds_addr_of(stA(s) + wave * 512), offA, k0 * kbA);
-    lds_copy16(rB, lds_addr_of(stB(s) + wave * 512), offB, k0 * kbB);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  static_for<0, SM_STAGES - 1>([&](auto s) { copy_slice(s, s); });
-  half8 fa[2], fb[2];
-  for (int kt = 0; kt < nk; kt += SM_STAGES) {
-    static_for<0, SM_STAGES>([&](auto U) {
-      constexpr int u = U;
-      const int sl = kt + u;
-      // own copies of slice sl done (two later slices may stay in flight),
-      // then every wave's
-      __builtin_amdgcn_s_waitcnt(vmcnt_wait(4) & ~0x0F00);
-      __builtin_amdgcn_s_barrier();
+  auto main_loop = [&](auto AK, auto BK) {
+    constexpr bool A_KM = decltype(AK)::value, B_KM = decltype(BK)::value;
+    const i32x4 rA = make_rsrc(d.A + static_cast<int64_t>(m0) * K, panel);
+    const i32x4 rB = make_rsrc(d.B + static_cast<int64_t>(n0) * K, panel);
+    const int row = wave * 16 + lane / 4;
+    const int col = ((lane % 4) ^ swz(row)) * 8;
+    const int kq = wave * 4 + (lane >> 4), ku = (lane >> 3) & 1;
+    uint32_t offA, offB;
+    if constexpr (A_KM) offA = static_cast<uint32_t>(km_src(kq, ku, lane & 7, d.M)) * 2u;
+    else offA = static_cast<uint32_t>(d.a_pairs ? (row >> 1) * 2 * K + (row & 1) * 32 + col
+                                                : row * K + col) * 2u;
+    if constexpr (B_KM) offB = static_cast<uint32_t>(km_src(kq, ku, lane & 7, d.N)) * 2u;
+    else offB = static_cast<uint32_t>(d.b_pairs ? (row >> 1) * 2 * K + (row & 1) * 32 + col
+                                                : row * K + col) * 2u;
+    const uint32_t kbA = d.a_pairs ? 4u : 2u, kbB = d.b_pairs ? 4u : 2u;
+    auto copy_slice = [&](int s, int sl) {
+      const uint32_t k0 = static_cast<uint32_t>(min(sl, nk - 1) * SM_BK);
+      if constexpr (A_KM) {
+        const i32x4 r = make_rsrc(d.A + 2 * static_cast<int64_t>(m0) + static_cast<int64_t>(k0) * d.M,
+                                  static_cast<uint32_t>(32 * d.M * 2));
+        lds_copy16(r, lds_addr_of(stA(s) + wave * 512), offA, 0u);
+      } else {
+        lds_copy16(rA, lds_addr_of(stA(s) + wave * 512), offA, k0 * kbA);
+      }
+      if constexpr (B_KM) {
+        const i32x4 r = make_rsrc(d.B + 2 * static_cast<int64_t>(n0) + static_cast<int64_t>(k0) * d.N,
+                                  static_cast<uint32_t>(32 * d.N * 2));
+        lds_copy16(r, lds_addr_of(stB(s) + wave * 512), offB, 0u);
+      } else {
+        lds_copy16(rB, lds_addr_of(stB(s) + wave * 512), offB, k0 * kbB);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      copy_slice((u + 3) % SM_STAGES, sl + 3);   // the stage of slice sl - 1, read by now
-      const _Float16* SA = stA(u);
-      const _Float16* SB = stB(u);
+    };
+    static_for<0, SM_STAGES - 1>([&](auto s) { copy_slice(s, s); });
+    half8 fa[2], fb[2];
+    for (int kt = 0; kt < nk; kt += SM_STAGES) {
+      static_for<0, SM_STAGES>([&](auto U) {
+        constexpr int u = U;
+        const int sl = kt + u;
+        // own copies of slice sl done (two later slices may stay in flight),
+        // then every wave's
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(4) & ~0x0F00);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        copy_slice((u + 3) % SM_STAGES, sl + 3);   // the stage of slice sl - 1, read by now
+        const _Float16* SA = stA(u);
+        const _Float16* SB = stB(u);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int kc = ks * 2 + (lane >> 5);
-        const int ra = wm * 32 + (lane & 31), rb = wn * 32 + (lane & 31);
-        fa[ks] = *reinterpret_cast<const half8*>(&SA[ra * SM_BK + ((kc ^ swz(ra)) * 8)]);
-        fb[ks] = *reinterpret_cast<const half8*>(&SB[rb * SM_BK + ((kc ^ swz(rb)) * 8)]);
-      }
-      if (fold && sl == fold_slice) {
-        const int rb = wn * 32 + (lane & 31);
-        const _Float16* base = SB + rb * SM_BK + 4 * (lane >> 5);
-        static_for<0, 4>([&](auto G) {
-          const half4 c = *reinterpret_cast<const half4*>(base + ((G ^ swz(rb)) * 8));
+        for (int ks = 0; ks < 2; ++ks) {
+          const int kc = ks * 2 + (lane >> 5);
+          const int ra = wm * 32 + (lane & 31), rb = wn * 32 + (lane & 31);
+          if constexpr (A_KM) fa[ks] = km_frag<2 * SM_TILE>(SA, wm * 32, ks, lane);
+          else fa[ks] = *reinterpret_cast<const half8*>(&SA[ra * SM_BK + ((kc ^ swz(ra)) * 8)]);
+          if constexpr (B_KM) fb[ks] = km_frag<2 * SM_TILE>(SB, wn * 32, ks, lane);
+          else fb[ks] = *reinterpret_cast<const half8*>(&SB[rb * SM_BK + ((kc ^ swz(rb)) * 8)]);
+        }
+        if constexpr (!B_KM) {
+          if (fold && sl == fold_slice) {
+            const int rb = wn * 32 + (lane & 31);
+            const _Float16* base = SB + rb * SM_BK + 4 * (lane >> 5);
+            static_for<0, 4>([&](auto G) {
+              const half4 c = *reinterpret_cast<const half4*>(base + ((G ^ swz(rb)) * 8));
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            acc[G * 4 + q] = __builtin_fmaf(rho, static_cast<float>(c[q]), acc[G * 4 + q]);
-        });
-      }
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[0], fb[0], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[1], fb[1], acc, 0, 0, 0);
-    });
+              for (int q = 0; q < 4; ++q)
+                acc[G * 4 + q] = __builtin_fmaf(rho, static_cast<float>(c[q]), acc[G * 4 + q]);
+            });
+          }
+        }
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[0], fb[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[1], fb[1], acc, 0, 0, 0);
+      });
+    }
+  };
+  if constexpr (KM) {
+    if (d.a_kmajor) main_loop(std::true_type{}, std::false_type{});
+    else if (d.b_kmajor) main_loop(std::false_type{}, std::true_type{});
+    else main_loop(std::false_type{}, std::false_type{});
+  } else {
+    main_loop(std::false_type{}, std::false_type{});
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));   // trailing copies
 
@@ -954,11 +1085,15 @@ int gemm_k_multiple() { return STAGES * MainCfg::BK; }
 
 int gemm_small_tile() { return SM_TILE; }
 
-hipError_t launch_gemm_small(const GemmDesc* descs, int count, int total_tiles,
+hipError_t launch_gemm_small(const GemmDesc* descs, int count, int total_tiles, bool kmajor,
                              hipStream_t stream) {
   if (total_tiles <= 0 || count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_small_kernel, dim3(total_tiles), dim3(SM_THREADS), 0, stream, descs,
-                     count, total_tiles);
+  if (kmajor)
+    hipLaunchKernelGGL(gemm_small_kernel<true>, dim3(total_tiles), dim3(SM_THREADS), 0, stream,
+                       descs, count, total_tiles);
+  else
+    hipLaunchKernelGGL(gemm_small_kernel<false>, dim3(total_tiles), dim3(SM_THREADS), 0, stream,
+                       descs, count, total_tiles);
   return hipGetLastError();
 }
 

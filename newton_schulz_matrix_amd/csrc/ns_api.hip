@@ -205,6 +205,7 @@ struct Stage {
   int count;    // descriptors
   int total;    // workgroups (chunks / tiles)
   bool small = false;   // GEMM on 64 x 64 tiles
+  bool kmajor = false;  // GEMM with a K-major operand in some descriptor
   double work;  // algorithmic flops (GEMM) or HBM bytes (normalisation)
 };
 
@@ -232,13 +233,17 @@ inline double gen_flops(int64_t m, int64_t n, int64_t k) { return 2.0 * m * n * 
 // is tall. Every entry point but the sharded one uses a single shard.
 struct Shard {
   int64_t c0, lc, Lp;      // first column, columns, padded columns
-  size_t X, XT[2], Rp;     // X_i (Sp x Lp), X_i^T (Lp x Sp) x2, partial Gram (Sp x Sp)
+  // Gram: X_i (Sp x Lp) twice (a restart writes Q X into the other one; the
+  // products by X read it K-major). Direct: X_i and X_i^T (Lp x Sp) twice
+  // (the step's product reads X^T and folds a X from it). Partial Gram
+  // matrix (Sp x Sp) of a sharded run.
+  size_t X[2], XT[2], Rp;
 };
 
 struct MatBuf {   // per-matrix workspace offsets (bytes from ws base)
   int64_t m, n, s, l, Sp, Lp;
   bool tall;
-  size_t X, XT[2], R, Z, T, Q[2], A, B;
+  size_t X, XT[2], R, Z, T, Q[2], A, B;   // X, XT: shard 0's (direct backend)
   std::vector<Shard> sh;
   int chunks, chunks_n, chunk_begin;
 };
@@ -261,8 +266,9 @@ size_t sq_bytes(int64_t r, int64_t c) { return static_cast<size_t>(r) * c * 2; }
 
 // Workspace layout: per-matrix fp16 buffers, chunk partials, norms, then
 // the descriptor table (its size depends only on count and params). With
-// shards > 1 (one matrix only) X, X^T and a partial Gram matrix exist per
-// shard; shard i has l / shards columns, one more for i < l % shards.
+// shards > 1 (one matrix only) the X buffers and a partial Gram matrix
+// exist per shard; shard i has l / shards columns, one more for
+// i < l % shards.
 void layout(Plan& pl, const ns_matrix* mats, int count, ns_backend be, int shards = 1) {
   size_t off = 0;
   pl.mats.resize(count);
@@ -286,13 +292,18 @@ void layout(Plan& pl, const ns_matrix* mats, int count, ns_backend be, int shard
       c0 += h.lc;
       h.Lp = pad_dim(h.lc);
       const size_t xl = sq_bytes(b.Sp, h.Lp);
-      h.X = off; off += xl;
-      h.XT[0] = off; off += xl;
-      h.XT[1] = off; off += xl;
+      h.X[0] = off; off += xl;
+      h.X[1] = h.XT[0] = h.XT[1] = 0;
+      if (be == NS_GRAM) {
+        h.X[1] = off; off += xl;
+      } else {
+        h.XT[0] = off; off += xl;
+        h.XT[1] = off; off += xl;
+      }
       h.Rp = 0;
       if (shards > 1) { h.Rp = off; off += ss; }
     }
-    b.X = b.sh[0].X;
+    b.X = b.sh[0].X[0];
     b.XT[0] = b.sh[0].XT[0];
     b.XT[1] = b.sh[0].XT[1];
     if (be == NS_GRAM) {
@@ -367,8 +378,13 @@ struct Builder {
       d.tile_begin = begin;
       begin += d.tiles;
     }
+    bool km = false;
+    for (auto& d : v) km = km || d.a_kmajor || d.b_kmajor;
     push(Stage::GEMM, v, begin, pr.flops);
-    if (!v.empty()) pl.stages.back().small = small;
+    if (!v.empty()) {
+      pl.stages.back().small = small;
+      pl.stages.back().kmajor = km;
+    }
   }
 
   // One launch of shard reductions (HBM-bound: every part read once, the
@@ -431,11 +447,12 @@ GemmDesc c_from_b(GemmDesc d) {
 inline size_t elem_bytes(ns_dtype t) { return t == NS_DT_F32 ? 4 : 2; }
 
 // Precision pipeline for every matrix: sum of squares and norm over the
-// whole matrix, then the scaled cast into X (short side first) and X^T,
-// zero-padded, per shard (a shard reads its own block of G and the whole
-// matrix's norm: the scalar all-reduce of a sharded run).
+// whole matrix, then the scaled cast into X (short side first; also X^T for
+// the direct backend), zero-padded, per shard (a shard reads its own block
+// of G and the whole matrix's norm: the scalar all-reduce of a sharded run).
 void norm_stages(Builder& B, const ns_matrix* mats, float eps) {
   Plan& pl = B.pl;
+  const bool with_xt = pl.backend != NS_GRAM;
   std::vector<NormDesc> v, cast;
   int tile_begin = 0;
   double read_bytes = 0.0, write_bytes = 0.0, momentum_bytes = 0.0;
@@ -443,7 +460,7 @@ void norm_stages(Builder& B, const ns_matrix* mats, float eps) {
     const MatBuf& b = pl.mats[i];
     const double elems = double(b.m) * double(b.n);
     read_bytes += elems * elem_bytes(mats[i].g_dtype);
-    write_bytes += elems * 2.0 * 2.0;
+    write_bytes += elems * 2.0 * (with_xt ? 2.0 : 1.0);
     if (pl.muon)   // the momentum pass also reads the gradient and writes M
       momentum_bytes += elems * (elem_bytes(pl.muon[i].grad_dtype) + elem_bytes(mats[i].g_dtype));
     NormDesc d{};
@@ -476,13 +493,13 @@ void norm_stages(Builder& B, const ns_matrix* mats, float eps) {
       if (!b.tall) {   // G is already short side first: G -> X, G^T -> X^T
         c.n = static_cast<int>(h.lc);
         c.pm = static_cast<int>(b.Sp); c.pn = static_cast<int>(h.Lp);
-        c.P = B.h(h.X); c.ldp = h.Lp;
-        c.PT = B.h(h.XT[0]); c.ldpt = b.Sp;
+        c.P = B.h(h.X[0]); c.ldp = h.Lp;
+        c.PT = with_xt ? B.h(h.XT[0]) : nullptr; c.ldpt = b.Sp;
       } else {         // tall: G -> X^T, G^T -> X
         c.m = static_cast<int>(h.lc);
         c.pm = static_cast<int>(h.Lp); c.pn = static_cast<int>(b.Sp);
-        c.P = B.h(h.XT[0]); c.ldp = b.Sp;
-        c.PT = B.h(h.X); c.ldpt = h.Lp;
+        c.P = with_xt ? B.h(h.XT[0]) : nullptr; c.ldp = b.Sp;
+        c.PT = B.h(h.X[0]); c.ldpt = h.Lp;
       }
       c.tiles_n = ceil_div(c.pn, CAST_TILE);
       c.tiles = ceil_div(c.pm, CAST_TILE) * c.tiles_n;
@@ -501,14 +518,22 @@ void norm_stages(Builder& B, const ns_matrix* mats, float eps) {
   B.push(Stage::CAST, cast, tile_begin, read_bytes + write_bytes);
 }
 
+// Marks operand A or B of a product as K-major (see GemmDesc).
+GemmDesc kmajor(GemmDesc d, bool a, bool b) {
+  d.a_kmajor = a ? 1 : 0;
+  d.b_kmajor = b ? 1 : 0;
+  return d;
+}
+
 void final_output(Builder& B, const ns_matrix& mt, const MatBuf& b, const Shard& h,
                   const _Float16* Qm, const _Float16* XT, const _Float16* Xc,
-                  const _Float16* XTc, float beta, Probs& out) {
+                  const _Float16* XTc, float beta, Probs& out, bool km = false) {
   // wide: out = Q X = Q (X^T)^T                    (M = Sp, N = Lp)
   // tall: out = (Q X)^T = X^T Q^T = X^T Q (Q sym.)  (M = Lp, N = Sp)
   // (direct backend: Q is the step matrix b A + c A^2 and the epilogue adds
   //  beta times X or X^T). A shard writes its own columns (wide) or rows
-  // (tall) of the caller's output.
+  // (tall) of the caller's output. km: the operand passed as XT is X
+  // itself, read K-major (right operand when wide, left when tall).
   const int ot = out_code(mt.out_dtype);
   const double f = gen_flops(b.s, h.lc, b.s);
   const Plan& pl = B.pl;
@@ -524,6 +549,7 @@ void final_output(Builder& B, const ns_matrix& mt, const MatBuf& b, const Shard&
                                 u.ld_param, b.m, h.lc, 0, ot, false, alpha, 1.f, 0.f, 0.f)
                          : gemm(XT, Qm, nullptr, w, nullptr, nullptr, h.Lp, b.Sp, b.Sp,
                                 u.ld_param, h.lc, b.n, 0, ot, false, alpha, 1.f, 0.f, 0.f);
+    g = kmajor(g, km && b.tall, km && !b.tall);
     g.C = w;
     g.ldc = static_cast<int>(u.ld_param);
     g.c_type = ot;
@@ -534,11 +560,12 @@ void final_output(Builder& B, const ns_matrix& mt, const MatBuf& b, const Shard&
   void* o = mt.out ? static_cast<unsigned char*>(mt.out) + static_cast<size_t>(h.c0) * step
                    : nullptr;
   if (!b.tall) {
-    out.add(c_from_b(gemm(Qm, XT, Xc, o, nullptr, nullptr, b.Sp, h.Lp, b.Sp, mt.ldo, b.m,
-                          h.lc, 0, ot, false, 1.f, beta, 0.f, 0.f)), f, true);
+    GemmDesc g = gemm(Qm, XT, Xc, o, nullptr, nullptr, b.Sp, h.Lp, b.Sp, mt.ldo, b.m, h.lc,
+                      0, ot, false, 1.f, beta, 0.f, 0.f);
+    out.add(km ? kmajor(g, false, true) : c_from_b(g), f, true);
   } else {
-    out.add(gemm(XT, Qm, XTc, o, nullptr, nullptr, h.Lp, b.Sp, b.Sp, mt.ldo, h.lc, b.n, 0,
-                 ot, false, 1.f, beta, 0.f, 0.f), f, true);
+    out.add(kmajor(gemm(XT, Qm, XTc, o, nullptr, nullptr, h.Lp, b.Sp, b.Sp, mt.ldo, h.lc, b.n,
+                        0, ot, false, 1.f, beta, 0.f, 0.f), km, false), f, true);
   }
 }
 
@@ -551,21 +578,23 @@ void gram_stages(Builder& B, const ns_matrix* mats, const ns_params& p) {
   // R = X X^T. A sharded matrix forms one partial Gram matrix per shard
   // (all shards in the same launch, as on separate devices), then their
   // shard-order sum: R = sum_i X_i X_i^T, the exact TP decomposition.
-  auto syrk_all = [&](int /*unused*/) {
+  // xc: which of the two X buffers holds the current X.
+  auto syrk_all = [&](int xc) {
     Probs v;
     std::vector<ReduceDesc> red;
     for (int i : pl.order) {
       const MatBuf& b = pl.mats[i];
       if (b.sh.size() == 1) {
-        v.add(gemm(B.h(b.X), B.h(b.X), nullptr, B.h(b.R), nullptr, nullptr, b.Sp, b.Sp, b.Lp,
+        const _Float16* X = B.h(b.sh[0].X[xc]);
+        v.add(gemm(X, X, nullptr, B.h(b.R), nullptr, nullptr, b.Sp, b.Sp, b.Lp,
                    b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, 0.f, 0.f, 0.f),
               sym_flops(b.s, b.l));
         continue;
       }
       ReduceDesc r{};
       for (const Shard& h : b.sh) {
-        v.add(gemm(B.h(h.X), B.h(h.X), nullptr, B.h(h.Rp), nullptr, nullptr, b.Sp, b.Sp, h.Lp,
-                   b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, 0.f, 0.f, 0.f),
+        v.add(gemm(B.h(h.X[xc]), B.h(h.X[xc]), nullptr, B.h(h.Rp), nullptr, nullptr, b.Sp,
+                   b.Sp, h.Lp, b.Sp, b.Sp, b.Sp, 0, OUT_F16, true, 1.f, 0.f, 0.f, 0.f),
               sym_flops(b.s, h.lc));
         r.parts[r.count++] = B.h(h.Rp);
       }
@@ -578,25 +607,27 @@ void gram_stages(Builder& B, const ns_matrix* mats, const ns_params& p) {
   };
 
   norm_stages(B, mats, p.eps);
-  syrk_all(0);
+  int xc = 0;
+  syrk_all(xc);
   bool q_identity = true;
-  int qc = 0, xt = 0;
+  int qc = 0;
   for (int k = 0; k < K; ++k) {
     const float a = p.coeffs[3 * k], bk = p.coeffs[3 * k + 1], ck = p.coeffs[3 * k + 2];
     if (restart[k] && !q_identity) {
-      // restart: X <- Q X (also written transposed), R <- X X^T, Q <- I
+      // restart: X <- Q X (X read K-major, the product written to the other
+      // X buffer), R <- X X^T, Q <- I
       Probs v;
       for (int i : pl.order) {
         const MatBuf& b = pl.mats[i];
         for (const Shard& h : b.sh)   // each shard applies Q to its own columns
-          v.add(gemm(B.h(b.Q[qc]), B.h(h.XT[xt]), nullptr, B.h(h.X), nullptr,
-                     B.h(h.XT[xt ^ 1]), b.Sp, h.Lp, b.Sp, h.Lp, b.Sp, h.Lp, 0, OUT_F16, false,
-                     1.f, 0.f, 0.f, 0.f),
+          v.add(kmajor(gemm(B.h(b.Q[qc]), B.h(h.X[xc]), nullptr, B.h(h.X[xc ^ 1]), nullptr,
+                            nullptr, b.Sp, h.Lp, b.Sp, h.Lp, b.Sp, h.Lp, 0, OUT_F16, false,
+                            1.f, 0.f, 0.f, 0.f), false, true),
                 gen_flops(b.s, h.lc, b.s));
       }
       B.gemm_stage(v);
-      xt ^= 1;
-      syrk_all(0);
+      xc ^= 1;
+      syrk_all(xc);
       q_identity = true;
     }
     const bool need_r = (k + 1 < K) && !restart[k + 1];
@@ -652,7 +683,8 @@ void gram_stages(Builder& B, const ns_matrix* mats, const ns_params& p) {
   for (int i : pl.order) {
     const MatBuf& b = pl.mats[i];
     for (const Shard& h : b.sh)
-      final_output(B, mats[i], b, h, B.h(b.Q[qc]), B.h(h.XT[xt]), nullptr, nullptr, 0.f, v);
+      final_output(B, mats[i], b, h, B.h(b.Q[qc]), B.h(h.X[xc]), nullptr, nullptr, 0.f, v,
+                   true);
   }
   B.gemm_stage(v);
 }
@@ -822,8 +854,18 @@ bool check_gemm(const GemmDesc& d, Bounds& B, int T) {
     return B.fail("gemm: valid block or diagonal outside the product");
   if (d.c_is_bt && (!d.C || d.M > d.K || d.alpha == 0.f))
     return B.fail("gemm: C folded from B needs C, M <= K and alpha != 0");
-  B.block("gemm A", d.A, d.M, d.K, d.K, d.a_pairs, 2, false);
-  B.block("gemm B", d.B, d.N, d.K, d.K, d.b_pairs, 2, false);
+  if (d.a_kmajor || d.b_kmajor) {
+    if (d.a_kmajor && d.b_kmajor) return B.fail("gemm: both operands K-major");
+    if (d.symmetric) return B.fail("gemm: K-major operand in a symmetric product");
+    if ((d.a_kmajor && !d.a_pairs) || (d.b_kmajor && !d.b_pairs))
+      return B.fail("gemm: K-major operand not in the row-pair layout");
+    if (d.b_kmajor && d.c_is_bt) return B.fail("gemm: C folded from a K-major B");
+  }
+  // a K-major operand is the (K x width) matrix read by pairs of k rows
+  if (d.a_kmajor) B.block("gemm A (K-major)", d.A, d.K, d.M, d.M, true, 2, false);
+  else B.block("gemm A", d.A, d.M, d.K, d.K, d.a_pairs, 2, false);
+  if (d.b_kmajor) B.block("gemm B (K-major)", d.B, d.K, d.N, d.N, true, 2, false);
+  else B.block("gemm B", d.B, d.N, d.K, d.K, d.b_pairs, 2, false);
   const void* C = d.c_is_bt ? nullptr : d.C;
   switch (epilogue_kind(d)) {
     case EK_SYM:
@@ -865,6 +907,8 @@ bool validate_plan(const Plan& pl, const unsigned char* ws, Bounds& B) {
         for (int i = 0; i < st.count; ++i) {
           if (d[i].tile_begin != next) return B.fail("gemm: tile ranges not contiguous");
           next += d[i].tiles;
+          if (st.small && !st.kmajor && (d[i].a_kmajor || d[i].b_kmajor))
+            return B.fail("gemm: K-major operand in a launch of the row-major-only kernel");
           if (!check_gemm(d[i], B, st.small ? gemm_small_tile() : gemm_tile())) return false;
         }
         if (next != st.total) return B.fail("gemm: launch size differs from its tiles");
@@ -942,9 +986,13 @@ void allow_buffers(Bounds& B, const Plan& pl, const unsigned char* ws, const ns_
     const size_t ss = sq_bytes(b.Sp, b.Sp);
     for (const Shard& h : b.sh) {
       const size_t xl = sq_bytes(b.Sp, h.Lp);
-      B.allow(ws + h.X, xl, true);
-      B.allow(ws + h.XT[0], xl, true);
-      B.allow(ws + h.XT[1], xl, true);
+      B.allow(ws + h.X[0], xl, true);
+      if (pl.backend == NS_GRAM) {
+        B.allow(ws + h.X[1], xl, true);
+      } else {
+        B.allow(ws + h.XT[0], xl, true);
+        B.allow(ws + h.XT[1], xl, true);
+      }
       if (b.sh.size() > 1) B.allow(ws + h.Rp, ss, true);
     }
     if (pl.backend == NS_GRAM) {
@@ -1104,7 +1152,7 @@ ns_status run_plan(const Plan& pl, unsigned char* ws, hipStream_t stream,
       case Stage::GEMM:
         e = timed(on, true, st.work, stream, [&] {
           const GemmDesc* d = reinterpret_cast<const GemmDesc*>(table + st.off);
-          return st.small ? launch_gemm_small(d, st.count, st.total, stream)
+          return st.small ? launch_gemm_small(d, st.count, st.total, st.kmajor, stream)
                           : launch_gemm(d, st.count, st.total, stream);
         });
         break;
@@ -1516,6 +1564,9 @@ ns_status grouped_desc(const ns_gemm_problem& q, GemmDesc& g) {
   if ((q.c_pairs && q.c && q.ldc % 32) || (q.d_pairs && q.ldd % 32)) return NS_ERR_INVALID_ARG;
   const bool fold = q.c_is_bt != 0;
   if (fold && (!q.c || q.M > q.K || q.alpha == 0.f)) return NS_ERR_INVALID_ARG;
+  if ((q.a_kmajor && q.b_kmajor) || ((q.a_kmajor || q.b_kmajor) && q.symmetric) ||
+      (q.a_kmajor && !q.a_pairs) || (q.b_kmajor && !q.b_pairs) || (q.b_kmajor && fold))
+    return NS_ERR_INVALID_ARG;
   const bool full16 = q.d_dtype == NS_DT_F16 && q.valid_m == q.M && q.valid_n == q.N &&
                       q.ldd % 8 == 0 && aligned16(q.d);
   if (q.symmetric) {
@@ -1541,6 +1592,8 @@ ns_status grouped_desc(const ns_gemm_problem& q, GemmDesc& g) {
   g.b_pairs = q.b_pairs ? 1 : 0;
   g.c_pairs = q.c_pairs ? 1 : 0;
   g.d_pairs = q.d_pairs ? 1 : 0;
+  g.a_kmajor = q.a_kmajor ? 1 : 0;
+  g.b_kmajor = q.b_kmajor ? 1 : 0;
   return NS_OK;
 }
 }  // namespace
@@ -1579,15 +1632,17 @@ NS_API ns_status ns_gemm_grouped(const ns_gemm_problem* probs, int count, int ti
   for (auto& d : v.d) big += d.tiles;
   const bool small = tile_edge ? tile_edge == gemm_small_tile() : big < SMALL_STAGE_TILES;
   int begin = 0;
+  bool km = false;
   for (auto& d : v.d) {
     if (small) set_tiles(d, gemm_small_tile());
     d.tile_begin = begin;
     begin += d.tiles;
+    km = km || d.a_kmajor || d.b_kmajor;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (upload(ws, v.d.data(), v.d.size() * sizeof(GemmDesc), st) != hipSuccess) return NS_ERR_HIP;
   const GemmDesc* dd = static_cast<const GemmDesc*>(ws);
-  if ((small ? launch_gemm_small(dd, count, begin, st) : launch_gemm(dd, count, begin, st)) !=
+  if ((small ? launch_gemm_small(dd, count, begin, km, st) : launch_gemm(dd, count, begin, st)) !=
       hipSuccess)
     return NS_ERR_HIP;
   return NS_OK;

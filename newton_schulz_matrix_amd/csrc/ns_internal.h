@@ -40,6 +40,13 @@ __host__ __device__ inline int64_t pair_index(int64_t i, int64_t j, int64_t ld) 
 // Layouts: a_pairs / b_pairs / c_pairs select the row-pair layout (leading
 // dimension K for A and B, N for C) instead of row-major; d_pairs does the
 // same for D (ld ldd), D2 (ld N) and DT (ld M).
+// K-major operands: a_kmajor stores A transposed, as a (K x M) matrix in the
+// row-pair layout with leading dimension M (element A[i][k] at
+// pair_index(k, i, M)); b_kmajor likewise B as (K x N) with leading
+// dimension N. This is how the iteration multiplies by X without keeping
+// X^T: Q X takes B = X (K-major), and (Q X)^T = X^T Q takes A = X. At most
+// one operand is K-major, never in the symmetric mode, and never B with
+// c_is_bt.
 // If c_is_bt: the caller guarantees C[i][j] == B[j][i] (C is B^T, which
 // needs M <= K), alpha != 0, and the kernel takes beta * C from the B
 // slices already in LDS during the K loop instead of reading C again.
@@ -63,6 +70,7 @@ struct GemmDesc {
   int symmetric;
   int c_is_bt;
   int a_pairs, b_pairs, c_pairs, d_pairs;
+  int a_kmajor, b_kmajor;
   int tile_begin;      // first logical tile of this problem in the launch
   int tiles;           // number of tiles of this problem
   int tiles_n;         // full: N / BN ; symmetric: M / BM
@@ -148,8 +156,9 @@ hipError_t launch_gemm(const GemmDesc* descs, int count, int total_tiles,
                        hipStream_t stream);
 // The same products on 64 x 64 tiles (tile counts and tile_begin of the
 // descriptors in units of 64 x 64 tiles, symmetric problems as the rows of
-// their lower triangle); bitwise the same results as launch_gemm.
-hipError_t launch_gemm_small(const GemmDesc* descs, int count, int total_tiles,
+// their lower triangle); bitwise the same results as launch_gemm. kmajor:
+// some descriptor has a K-major operand (selects the kernel that reads them).
+hipError_t launch_gemm_small(const GemmDesc* descs, int count, int total_tiles, bool kmajor,
                              hipStream_t stream);
 int gemm_small_tile();
 hipError_t launch_reduce(const ReduceDesc* descs, int count, int total_blocks,

@@ -84,8 +84,15 @@ def test_workspace_size_monotone_and_additive():
     assert _size([(1, 1)]) == _size([(200, 250)])
     # tall and wide of the same pair use the same short-side buffers
     assert _size([(1024, 256)]) == _size([(256, 1024)])
-    # direct needs fewer Gram-sized buffers than gram
-    assert _size([(1024, 4096)], "direct", restarts=()) < _size([(1024, 4096)])
+    # buffer counts: gram keeps X twice (s x l) and R, Z, T, Q, Q' (s x s);
+    # direct keeps X, X^T twice and A, B. The difference between the two
+    # backends is one s x l buffer less three s x s ones, plus table bytes.
+    s, l = 1024, 4096
+    diff = _size([(s, l)], "direct", restarts=()) - _size([(s, l)])
+    assert abs(diff - (s * l - 3 * s * s) * 2) < 64 * 1024
+    # and one more column block of 256 adds two s x 256 fp16 buffers to gram
+    grow = _size([(s, l + 256)]) - _size([(s, l)])
+    assert abs(grow - 2 * s * 256 * 2) < 4096
 
 
 def test_workspace_size_llama_owner_batch_fits():

@@ -5,8 +5,9 @@ ns_gemm_grouped exposes every descriptor option the stage planner uses: the
 row-pair layout of internal buffers, beta * C folded from the B slices
 (C == B^T), the second output D2 = D + delta I of the first Z product after a
 start or restart, the transposed second output DT of the restart product,
-symmetric (lower-tile + mirror) mode, and the clipped, typed epilogue that
-writes a caller's buffer. Each launch holds more than 256 tiles, so the XCD
+symmetric (lower-tile + mirror) mode, the clipped, typed epilogue that
+writes a caller's buffer, and K-major operands (X read as the right operand
+of Q X, or as the left operand of X^T Q, from its own row-pair buffer). Each launch holds more than 256 tiles, so the XCD
 remapping of workgroup ids and the banded tile walks (several bands of tile
 rows, lower-triangle bands for symmetric products) are all exercised. Shapes
 are the Llama-3-8B owner batch's: SYRK 4096 x 14336, symmetric 4096^3 Gram-
@@ -191,6 +192,43 @@ def test_qx_with_transposed_output_and_fold():
                  "Q X + a X")
 
 
+def test_kmajor_operands():
+    """The Gram iteration's products by X without X^T: Q X with X read as a
+    K-major right operand (Q 4096^2, X 4096 x 14336, fp16 row-pair output,
+    896 tiles), and in the same launch X2^T Q2 with X2 (1024 x 8192) read as
+    a K-major left operand into a caller's bf16 buffer, clipped, with an fp32
+    C read in the epilogue and a negative alpha (the Muon update's form)."""
+    require_gpu()
+    print("K-major QX 4096 x 4096 x 14336 + X^T Q 8192 x 1024 x 1024", flush=True)
+    Qm = rand16((4096, 4096), 1.0 / np.sqrt(4096), 30)
+    X = rand16((4096, 14336), 1.0, 31)
+    D = torch.empty((4096, 14336), dtype=torch.float16, device="cuda")
+    Q2 = rand16((1024, 1024), 1.0 / np.sqrt(1024), 32)
+    X2 = rand16((1024, 8192), 1.0, 33)
+    vm, vn, ldd = 8000, 1000, 1001
+    W = torch.randn((vm, ldd), device="cuda")
+    Dt = torch.full((vm, ldd), 7.0, dtype=torch.bfloat16, device="cuda")
+    alpha = -0.02
+    nsmi.ns_gemm_grouped([
+        dict(a=to_pairs(Qm), b=to_pairs(X), d=D, M=4096, N=14336, K=4096, a_pairs=1, b_pairs=1,
+             d_pairs=1, b_kmajor=1),
+        dict(a=to_pairs(X2), b=to_pairs(Q2), c=W, d=Dt, M=8192, N=1024, K=1024, ldc=ldd,
+             ldd=ldd, valid_m=vm, valid_n=vn, a_pairs=1, b_pairs=1, a_kmajor=1, alpha=alpha,
+             beta=1.0),
+    ])
+    torch.cuda.synchronize()
+    Q64, X64 = to64(Qm), to64(X)
+    assert_bound(to64(from_pairs(D)), Q64 @ X64, acc_bound(4096, 1.0, Q64, X64.T),
+                 torch.float16, "Q X, X K-major")
+    A64, B64 = to64(X2).T[:vm], to64(Q2)[:vn]
+    C64 = to64(W)[:, :vn]
+    got = to64(Dt)
+    assert_bound(got[:, :vn], alpha * (A64 @ B64.T) + C64,
+                 acc_bound(1024, alpha, A64, B64, 1.0, C64), torch.bfloat16,
+                 "X^T Q, X K-major, clipped")
+    assert np.all(got[:, vn:] == 7.0)
+
+
 @pytest.mark.parametrize("d_dtype,c_dtype", [(torch.bfloat16, torch.float32),
                                              (torch.float32, torch.bfloat16),
                                              (torch.float16, torch.float16)])
@@ -241,8 +279,9 @@ def test_clipped_caller_buffers(d_dtype, c_dtype):
 def _path_problems(seed):
     """One problem per epilogue path, at sizes both kernels tile: symmetric
     with fold and D2, symmetric with C read in the epilogue, SYRK, full with
-    fold and the transposed output, and clipped caller buffers of each type
-    combination."""
+    fold and the transposed output, clipped caller buffers of each type
+    combination, and both K-major operand forms (Q X into a row-pair buffer,
+    X^T Q into a clipped caller buffer with C)."""
     S = sym16(512, seed)
     T = sym16(512, seed + 1)
     X = rand16((512, 1024), 1.0 / 32, seed + 2)
@@ -257,7 +296,8 @@ def _path_problems(seed):
         e = lambda *sh, dt=torch.float16: torch.full(sh, 5.0, dtype=dt, device="cuda")
         return dict(z=e(512, 512), q=e(512, 512), r=e(512, 512), syrk=e(512, 512),
                     x=e(512, 1024), xt=e(1024, 512), cl1=e(300, 703, dt=torch.bfloat16),
-                    cl2=e(300, 703, dt=torch.float32), cl3=e(300, 703))
+                    cl2=e(300, 703, dt=torch.float32), cl3=e(300, 703),
+                    kx=e(512, 1024), kt=e(1000, 703, dt=torch.bfloat16))
     def probs(o):
         return [
             dict(a=Sp, b=Sp, c=Sp, d=o["z"], d2=o["q"], M=512, N=512, K=512, symmetric=1,
@@ -277,6 +317,11 @@ def _path_problems(seed):
                  valid_m=300, valid_n=700, diag_n=300, alpha=-0.02, beta=1.0),
             dict(a=A, b=Bm, d=o["cl3"], M=512, N=768, K=384, ldd=703, valid_m=300,
                  valid_n=700, diag_n=0, alpha=1.0),
+            dict(a=to_pairs(Q), b=Xp, d=o["kx"], M=512, N=1024, K=512, a_pairs=1, b_pairs=1,
+                 d_pairs=1, b_kmajor=1),
+            dict(a=Xp, b=to_pairs(Q), c=C32, d=o["kt"], M=1024, N=512, K=512, ldc=701, ldd=703,
+                 valid_m=300, valid_n=500, a_pairs=1, b_pairs=1, a_kmajor=1, alpha=-0.02,
+                 beta=1.0),
         ]
     return outs, probs
 
@@ -298,3 +343,13 @@ def test_small_tile_kernel_gives_the_same_bits(seed):
         assert torch.equal(big[k], small[k]), k
     for k in ("cl1", "cl2", "cl3"):
         assert torch.all(big[k][:, 700:].float() == 5.0), k
+    assert torch.all(big["kt"][300:].float() == 5.0) and torch.all(big["kt"][:, 500:].float() == 5.0)
+    # the K-major products are the products (not only the same in both kernels)
+    pk = probs(big)
+    Q64, X64 = to64(from_pairs(pk[7]["a"])), to64(from_pairs(pk[7]["b"]))
+    assert_bound(to64(from_pairs(big["kx"])), Q64 @ X64, acc_bound(512, 1.0, Q64, X64.T),
+                 torch.float16, "Q X, X K-major")
+    A64, B64, C64 = X64.T[:300], Q64[:500], to64(pk[8]["c"])[:300, :500]
+    assert_bound(to64(big["kt"])[:300, :500], -0.02 * (A64 @ B64.T) + C64,
+                 acc_bound(512, -0.02, A64, B64, 1.0, C64), torch.bfloat16,
+                 "X^T Q, X K-major, clipped")

@@ -88,3 +88,63 @@ def test_single_matrix_workload_replays_bitwise():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(og, eg) and torch.equal(od, ed)
+
+
+def test_sharded_call_replays_bitwise():
+    """The column-sharded route (4 virtual shards, shard reduction kernel)
+    captured; its output and workspace come from the graph's memory pool."""
+    require_gpu()
+    G = W.small_gaussian(90, 384, 1536).cuda()
+    co = nsmi.POLAR_EXPRESS_COEFFICIENTS
+    holder = {}
+
+    def call():
+        holder["out"] = nsmi.ns_gram_sharded(G, 4, co, (2,))
+
+    g = _capture(call)
+    out = holder["out"]
+    for rep in range(3):
+        G.copy_(W.small_gaussian(91 + rep, 384, 1536).cuda())
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        want = nsmi.ns_gram_sharded(G, 4, co, (2,))
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), rep
+
+
+def test_muon_step_replays_bitwise():
+    """ns_muon_step updates momentum and parameters in place; before each
+    replay the state is restored, and the replayed state must equal an eager
+    step from the same state."""
+    require_gpu()
+    shapes = [(256, 1024), (1024, 256), (300, 500)]
+    grads = [W.small_gaussian(100 + i, *sh).cuda().to(torch.bfloat16)
+             for i, sh in enumerate(shapes)]
+    m0 = [W.small_gaussian(110 + i, *sh).cuda().float() for i, sh in enumerate(shapes)]
+    w0 = [W.small_gaussian(120 + i, *sh).cuda().float() for i, sh in enumerate(shapes)]
+    mom = [m.clone() for m in m0]
+    par = [w.clone() for w in w0]
+    co = nsmi.POLAR_EXPRESS_COEFFICIENTS
+    ws = torch.empty(1 << 26, dtype=torch.uint8, device="cuda")
+
+    def call():
+        nsmi.ns_muon_step(grads, mom, par, 0.95, 0.02, coefficients=co,
+                          restart_iterations=(2,), workspace=ws)
+
+    g = _capture(call)
+    for rep in range(3):
+        for a, b in zip(mom + par, m0 + w0):
+            a.copy_(b)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in mom + par]
+        em = [m.clone() for m in m0]
+        ew = [w.clone() for w in w0]
+        nsmi.ns_muon_step(grads, em, ew, 0.95, 0.02, coefficients=co, restart_iterations=(2,))
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(got, em + ew)):
+            assert torch.equal(a, b), (rep, i)
