@@ -351,3 +351,39 @@ def test_binding_checks_shapes_and_types_before_device_work():
         nsmi.ns_gemm_nt(torch.zeros(256, 128), h(256, 128))
     with pytest.raises(ValueError, match="fp16"):
         nsmi.ns_syrk(torch.zeros(256, 128))
+
+
+def _grouped(**kw):
+    """One ns_gemm_grouped problem with fake, aligned, never-dereferenced
+    pointers; returns the status (arguments are checked before any device
+    work, so a valid problem reaches the device check)."""
+    base = dict(a=0x10000, b=0x20000, c=None, d=0x30000, d2=None, dt=None, M=256, N=512,
+                K=256, ldc=512, ldd=512, valid_m=256, valid_n=512, diag_n=0,
+                c_dtype=nsmi.NS_DT_F16, d_dtype=nsmi.NS_DT_F16, symmetric=0, c_is_bt=0,
+                a_pairs=1, b_pairs=1, c_pairs=0, d_pairs=0, a_kmajor=0, b_kmajor=0,
+                alpha=1.0, beta=0.0, gamma=0.0, delta=0.0)
+    base.update(kw)
+    p = nsmi._GemmProblem(**base)
+    return nsmi.library().ns_gemm_grouped(ctypes.byref(p), 1, 0, ctypes.c_void_p(0x40000),
+                                          ctypes.c_size_t(1 << 20), None)
+
+
+def test_gemm_grouped_kmajor_rules():
+    """K-major operands: at most one, in the row-pair layout, not in the
+    symmetric mode and not a B whose transpose is folded in as C."""
+    ok = {nsmi.NS_OK, nsmi.NS_ERR_UNSUPPORTED, nsmi.NS_ERR_HIP}
+    assert _grouped(b_kmajor=1) in ok
+    assert _grouped(a_kmajor=1) in ok
+    bad = nsmi.NS_ERR_INVALID_ARG
+    assert _grouped(a_kmajor=1, b_kmajor=1) == bad
+    assert _grouped(b_kmajor=1, b_pairs=0) == bad
+    assert _grouped(a_kmajor=1, a_pairs=0) == bad
+    sym = dict(M=512, valid_m=512, symmetric=1)
+    assert _grouped(**sym) in ok
+    assert _grouped(a_kmajor=1, **sym) == bad
+    assert _grouped(b_kmajor=1, **sym) == bad
+    fold = dict(N=256, valid_n=256, c=0x50000, ldc=256, ldd=256, beta=1.0, c_is_bt=1)
+    assert _grouped(b_kmajor=1, **fold) == bad
+    # the same fold with a row-major B, or with a K-major A, is accepted
+    assert _grouped(**fold) in ok
+    assert _grouped(a_kmajor=1, **fold) in ok
