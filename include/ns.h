@@ -360,6 +360,7 @@ ns_status ns_gemm_grouped(const ns_gemm_problem* probs, int count, int tile_edge
  *   4 the cast writing 64 rows past its padded block
  *   5 the norm pass reading one row past the input
  *   6 a shard reduction running one block past its parts
+ *   7 a product reading its K-major operand from one K block further on
  * Returns NS_OK, NS_ERR_INTERNAL (first violation described in msg, if msg
  * is not NULL, truncated to msg_len bytes), or the status the entry point's
  * argument checks give. */

@@ -1028,6 +1028,7 @@ enum Plant {
   PLANT_CAST_ROWS = 4,      // the cast writes 64 rows past its padded block
   PLANT_SUMSQ_ROW = 5,      // the norm pass reads one row past G
   PLANT_REDUCE_TAIL = 6,    // a shard reduction runs one block past its parts
+  PLANT_KMAJOR_K = 7,       // a K-major operand read from one K block further on
 };
 bool plant_mistake(Plan& pl, const unsigned char* ws, size_t ws_bytes, int plant) {
   auto in_ws = [&](const void* p) {
@@ -1053,6 +1054,14 @@ bool plant_mistake(Plan& pl, const unsigned char* ws, size_t ws_bytes, int plant
         }
         if (plant == PLANT_K_OVERRUN) {
           g.K += gemm_k_multiple();
+          return true;
+        }
+        if (plant == PLANT_KMAJOR_K && (g.a_kmajor || g.b_kmajor)) {
+          // the K-major operand's rows start one K block later (its other
+          // operand unchanged)
+          const int64_t rows = gemm_k_multiple();
+          if (g.a_kmajor) g.A += rows * g.M;
+          else g.B += rows * g.N;
           return true;
         }
       }

@@ -30,7 +30,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(nsmi.LIB_PATH),
                                 reason="libnsmi.so not built")
 
 ES = {nsmi.NS_DT_F32: 4, nsmi.NS_DT_BF16: 2, nsmi.NS_DT_F16: 2}
-PLANTS = range(1, 7)
+PLANTS = range(1, 8)
 
 
 class Arena:
@@ -160,3 +160,14 @@ def test_small_workspace_and_misaligned_workspace_refused():
     assert st == nsmi.NS_ERR_WORKSPACE
     st, _ = nsmi.ns_plan_check(entry, mats, be, sh, nsmi.YOU_COEFFICIENTS, rs, ws=(1 << 40) + 8)
     assert st == nsmi.NS_ERR_WORKSPACE
+
+
+def test_kmajor_operand_overrun_is_named():
+    """The products by X read it K-major (K x width, by pairs of k rows); read
+    one K block further they run past the X buffer, and the check names the
+    K-major operand."""
+    for name in ("gram ragged", "gram ld>n", "sharded wide x7", "sharded tall x64",
+                 "muon ragged"):
+        st, msg = check(*CASES[name], plant=7)
+        assert st == nsmi.NS_ERR_INTERNAL, (name, st, msg)
+        assert "K-major" in msg, (name, msg)
