@@ -42,9 +42,10 @@
 //     row-pair layout, see km_off): X serves as the right operand of Q X,
 //     or as the left one of X^T Q, without a transposed copy; its slices
 //     are copied by pairs of k rows and read with transposing LDS reads;
-//   * on a diagonal tile of a symmetric product group 0's four waves split
-//     the 128 stored columns of their rows (32 each) rather than two of them
-//     computing the never-stored upper-right quadrant;
+//   * a diagonal tile of a symmetric product computes only its 36 stored
+//     32 x 32 blocks (on or below the diagonal), 5 per wave of group 1 and 4
+//     per wave of group 0 (diag_block), so its two MFMA phases per K slice
+//     issue 10 and 8 MFMAs instead of 16 and 16;
 //   * epilogue arithmetic is written out (explicit fused multiply-adds, the
 //     fp32 value held before its conversion), so every code path computing
 //     an element rounds it the same way.
@@ -408,6 +409,28 @@ __device__ __forceinline__ half8 km_frag(const _Float16* S, int col, int ks, int
   return __builtin_bit_cast(half8, x);
 }
 
+// Diagonal tile of a symmetric product: of its 8 x 8 blocks of 32 x 32 only
+// the 36 with row block bi >= column block bj are stored (the others are
+// their mirror). Wave wn of group 1 takes blocks (wn .. wn + 4, wn); wave wn
+// of group 0 takes the rest of column wn, rows wn + 5 .. 7 (3 - wn blocks),
+// and column 7 - wn, rows 7 - wn .. 7 (wn + 1 blocks): 5 + 4 blocks per pair
+// of waves, so the two MFMA phases of a K slice issue 10 and 8 MFMAs.
+__device__ __forceinline__ void diag_block(int grp, int wn, int b, int& bi, int& bj) {
+  if (grp == 1) {
+    bi = wn + b;
+    bj = wn;
+    return;
+  }
+  const int na = 3 - wn;
+  if (b < na) {
+    bi = wn + 5 + b;
+    bj = wn;
+  } else {
+    bj = 7 - wn;
+    bi = bj + (b - na);
+  }
+}
+
 enum EpiMode { EPI_SYM_OFFDIAG, EPI_SYM_DIAG, EPI_FULL, EPI_FULL_C };
 
 // Fast epilogue for fp16 outputs inside internal (padded, aligned) buffers:
@@ -425,19 +448,26 @@ template <class Cf, int MODE, class Acc>
 __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Float16* S,
                                               float* sdiag, int lane, int wm, int wn,
                                               int m0, int n0, _Float16* T, int ldT,
-                                              _Float16* T2, bool half_cols = false) {
+                                              _Float16* T2) {
   static_assert(Cf::BM == 256 && Cf::BN == 256, "tile-wide staging is 256 x 256");
   constexpr bool SYM = MODE == EPI_SYM_OFFDIAG || MODE == EPI_SYM_DIAG;
   lds_char* const Sl = (lds_char*)(S);
   const int h = lane >> 5;
   static_for<0, Cf::FM>([&](auto I) {
     static_for<0, Cf::FN>([&](auto J) {
-      // group 0 of a diagonal tile computed one 32-column block per wave
-      if (MODE == EPI_SYM_DIAG && half_cols && J > 0) return;
+      int brow = wm * Cf::WM + I * 32, bcol = wn * Cf::WN + J * 32;
+      if constexpr (MODE == EPI_SYM_DIAG) {
+        // diagonal tile: accumulator slot I + 4 J holds block diag_block(.)
+        constexpr int b = I + 4 * J;
+        if (b >= (wm == 1 ? 5 : 4)) return;
+        int bi, bj;
+        diag_block(wm, wn, b, bi, bj);
+        brow = bi * 32;
+        bcol = bj * 32;
+      }
       const floatx16& a = acc[I][J];
-      const int lcol = (MODE == EPI_SYM_DIAG && half_cols ? wn * 32 : wn * Cf::WN) + J * 32 +
-                       (lane & 31);                              // tile-local column
-      const int lrow0 = wm * Cf::WM + I * 32;                   // tile-local block row
+      const int lcol = bcol + (lane & 31);                      // tile-local column
+      const int lrow0 = brow;                                   // tile-local block row
       const int col = n0 + lcol, rbase = m0 + lrow0;            // global
       uint32_t P[4][2];
       static_for<0, 2>([&](auto GP) {
@@ -581,13 +611,11 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  // On a diagonal tile of a symmetric product only the lower triangle is
-  // stored (the upper one is its mirror); group 0 (tile rows 0-127) then
-  // needs columns 0-127 only, and its four waves split them (32 columns
-  // each) instead of two of them computing the never-stored upper-right
-  // quadrant: half the MFMAs for group 0, the same value for every element.
-  const bool half_cols = sym && ti == tj && wm == 0;
-  const int bcol0 = half_cols ? wn * 32 : wn * C::WN;   // first column of this wave's blocks
+  // A diagonal tile of a symmetric product computes only its stored blocks,
+  // dealt out over the waves by diag_block; every element gets the same
+  // arithmetic as in any other tile.
+  const bool diag = sym && ti == tj;
+  const int bcol0 = wn * C::WN;   // first column of this wave's blocks (other tiles)
 
   // beta * C taken from the B slices (C == B^T): global row i of C is
   // column k = i of B, so this wave's 32-row block I arrives with K slice
@@ -677,16 +705,40 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
         }
       });
       static_for<0, C::FN>([&](auto J) {
-        if (J == 0 || !half_cols) {
-          if constexpr (decltype(BK)::value) {
-            fb[KS][J] = km_frag<KM_PAIR>(SB, bcol0 + J * 32, KS, lane);
-          } else {
-            const int row = bcol0 + J * 32 + (lane & 31);
-            fb[KS][J] =
-                *reinterpret_cast<const half8*>(&SB[row * C::BK + ((kc ^ swz(row)) * 8)]);
-          }
+        if constexpr (decltype(BK)::value) {
+          fb[KS][J] = km_frag<KM_PAIR>(SB, bcol0 + J * 32, KS, lane);
+        } else {
+          const int row = bcol0 + J * 32 + (lane & 31);
+          fb[KS][J] = *reinterpret_cast<const half8*>(&SB[row * C::BK + ((kc ^ swz(row)) * 8)]);
         }
       });
+    });
+  };
+  // Diagonal-tile fragments, G = the wave's group. Group 1: A rows of blocks
+  // wn .. wn + 3 in fa, of block wn + 4 in fb[.][1], B columns of block
+  // column wn in fb[.][0]. Group 0: A rows of its four blocks in fa, B
+  // columns of block columns wn and 7 - wn in fb[.][0] and fb[.][1].
+  auto frag_at = [&](const _Float16* S, int row0, int kc) {
+    const int row = row0 + (lane & 31);
+    return *reinterpret_cast<const half8*>(&S[row * C::BK + ((kc ^ swz(row)) * 8)]);
+  };
+  auto read_frags_diag = [&](const _Float16* SA, const _Float16* SB, auto& fa, auto& fb,
+                             auto G) {
+    static_for<0, C::KSTEPS>([&](auto KS) {
+      const int kc = KS * 2 + (lane >> 5);
+      if constexpr (decltype(G)::value == 1) {
+        static_for<0, 4>([&](auto B) { fa[KS][B] = frag_at(SA, (wn + B) * 32, kc); });
+        fb[KS][1] = frag_at(SA, (wn + 4) * 32, kc);
+        fb[KS][0] = frag_at(SB, wn * 32, kc);
+      } else {
+        static_for<0, 4>([&](auto B) {
+          int bi, bj;
+          diag_block(0, wn, B, bi, bj);
+          fa[KS][B] = frag_at(SA, bi * 32, kc);
+        });
+        fb[KS][0] = frag_at(SB, wn * 32, kc);
+        fb[KS][1] = frag_at(SB, (7 - wn) * 32, kc);
+      }
     });
   };
   auto mfmas = [&](auto& fa, auto& fb) {
@@ -699,31 +751,61 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
       });
     });
   };
-  // group 0 of a diagonal tile: one column block per wave
-  auto mfmas_half = [&](auto& fa, auto& fb) {
-    static_for<0, C::KSTEPS>([&](auto KS) {
-      static_for<0, C::FM>([&](auto I) {
-        acc[I][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[KS][I], fb[KS][0], acc[I][0],
+  // Diagonal tile: block b accumulates in acc[b % 4][b / 4]. Group 0's
+  // blocks b < 3 - wn use B column wn, the others 7 - wn; the split is
+  // chosen once per phase so the MFMA stream stays one straight-line block.
+  auto mfmas_diag = [&](auto& fa, auto& fb, auto G) {
+    if constexpr (decltype(G)::value == 1) {
+      static_for<0, C::KSTEPS>([&](auto KS) {
+        static_for<0, 4>([&](auto B) {
+          acc[B][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[KS][B], fb[KS][0], acc[B][0],
+                                                             0, 0, 0);
+        });
+        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[KS][1], fb[KS][0], acc[0][1],
                                                            0, 0, 0);
       });
-    });
+    } else {
+      auto seq = [&](auto NA) {
+        static_for<0, C::KSTEPS>([&](auto KS) {
+          static_for<0, 4>([&](auto B) {
+            constexpr int j = B < decltype(NA)::value ? 0 : 1;
+            acc[B][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[KS][B], fb[KS][j], acc[B][0],
+                                                               0, 0, 0);
+          });
+        });
+      };
+      if (wn == 0) seq(std::integral_constant<int, 3>{});
+      else if (wn == 1) seq(std::integral_constant<int, 2>{});
+      else if (wn == 2) seq(std::integral_constant<int, 1>{});
+      else seq(std::integral_constant<int, 0>{});
+    }
   };
   // acc[I][J] += rho * C for the 32 rows of block I, read from slice SB:
   // lane l needs rows 8g + 4(l/32) .. +3 (g = 0..3) of column l%32 of block
   // J, i.e. four consecutive k of B row (block J column), 8 bytes.
-  auto fold_c = [&](const _Float16* SB, auto I) {
-    static_for<0, C::FN>([&](auto J) {
-      if (J == 0 || !half_cols) {
-        const int row = bcol0 + J * 32 + (lane & 31);
-        const _Float16* base = SB + row * C::BK + 4 * (lane >> 5);
-        static_for<0, 4>([&](auto G) {
-          const half4 c = *reinterpret_cast<const half4*>(base + ((G ^ swz(row)) * 8));
+  auto fold_block = [&](const _Float16* SB, int col0, floatx16& a) {
+    const int row = col0 + (lane & 31);
+    const _Float16* base = SB + row * C::BK + 4 * (lane >> 5);
+    static_for<0, 4>([&](auto G) {
+      const half4 c = *reinterpret_cast<const half4*>(base + ((G ^ swz(row)) * 8));
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            acc[I][J][G * 4 + q] =
-                __builtin_fmaf(rho, static_cast<float>(c[q]), acc[I][J][G * 4 + q]);
-        });
-      }
+      for (int q = 0; q < 4; ++q)
+        a[G * 4 + q] = __builtin_fmaf(rho, static_cast<float>(c[q]), a[G * 4 + q]);
+    });
+  };
+  auto fold_c = [&](const _Float16* SB, auto I) {
+    static_for<0, C::FN>([&](auto J) { fold_block(SB, bcol0 + J * 32, acc[I][J]); });
+  };
+  // Diagonal tile: block (bi, bj) takes beta * C from the slice holding its
+  // rows, slice 8 ti + bi = ring round 2 ti + bi / 4, position bi % 4.
+  auto fold_diag = [&](const _Float16* SB, auto POS, int round, auto G) {
+    if (!fold || (round >> 1) != ti) return;
+    constexpr int NB = decltype(G)::value == 1 ? 5 : 4;
+    static_for<0, NB>([&](auto B) {
+      int bi, bj;
+      diag_block(decltype(G)::value, wn, B, bi, bj);
+      if ((bi & 3) == decltype(POS)::value && 2 * ti + (bi >> 2) == round)
+        fold_block(SB, bj * 32, acc[B % 4][B / 4]);
     });
   };
   // Ping-pong schedule, one barrier per phase. On every SIMD one wave of
@@ -742,20 +824,28 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // HALF: group 0 of a diagonal tile (chosen once per tile, so that the
-  // MFMA stream of a phase stays one straight-line block)
-  auto mfma_phase = [&](auto& fa, auto& fb, auto HALF) {
-    if constexpr (decltype(HALF)::value) mfmas_half(fa, fb);
+  // DIAG: a diagonal tile (chosen once per tile, so that the MFMA stream of
+  // a phase stays one straight-line block); G: the wave's group
+  auto mfma_phase = [&](auto& fa, auto& fb, auto DIAG, auto G) {
+    if constexpr (decltype(DIAG)::value) mfmas_diag(fa, fb, G);
     else mfmas(fa, fb);
     __builtin_amdgcn_sched_barrier(0);
+  };
+  auto read_phase = [&](const _Float16* SA, const _Float16* SB, auto& fa, auto& fb, auto DIAG,
+                        auto AK, auto BK, auto G) {
+    if constexpr (decltype(DIAG)::value) read_frags_diag(SA, SB, fa, fb, G);
+    else read_frags(SA, SB, fa, fb, AK, BK);
   };
   // K is a multiple of STAGES * BK; requests past the last slice re-read the
   // last slice into a stage that is never consumed again.
   const int nk = K / C::BK;
   auto kclamp = [&](int sl) { return min(sl, nk - 1) * C::BK; };
-  // HALF as above; AK / BK: A / B is K-major (at most one; never with HALF).
+  // DIAG as above; AK / BK: A / B is K-major (at most one; never with DIAG).
   // The fold is compiled only where B slices are row-major.
-  auto k_loop = [&](auto HALF, auto AK, auto BK) {
+  auto k_loop = [&](auto DIAG, auto AK, auto BK) {
+  constexpr bool IS_DIAG = decltype(DIAG)::value;
+  const std::integral_constant<int, 0> G0;
+  const std::integral_constant<int, 1> G1;
   constexpr bool FOLD_OK = !decltype(BK)::value;
   if (grp == 0) static_for<0, STAGES>([&](auto s) { copy_my(s, kclamp(s), AK); });
   else static_for<0, STAGES>([&](auto s) { copy_my(s, kclamp(s), BK); });
@@ -763,8 +853,9 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * COPIES) & ~0x0F00);
   __builtin_amdgcn_s_barrier();
   if (grp == 0) {
-    read_frags(stA(0), stB(0), fa0, fb0, AK, BK);
-    if constexpr (FOLD_OK)
+    read_phase(stA(0), stB(0), fa0, fb0, DIAG, AK, BK, G0);
+    if constexpr (IS_DIAG) fold_diag(stB(0), std::integral_constant<int, 0>{}, 0, G0);
+    else if constexpr (FOLD_OK)
       if (fold_round == 0) fold_c(stB(0), std::integral_constant<int, 0>{});
     phase_end();
     for (int kt = 0; kt < nk; kt += STAGES) {
@@ -774,11 +865,14 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
         auto& fb = fb0;
         auto& fan = fa0;
         auto& fbn = fb0;
-        mfma_phase(fa, fb, HALF);
+        mfma_phase(fa, fb, DIAG, G0);
         phase_end();
         copy_my(u, kclamp(kt + u + 4), AK);
-        read_frags(stA((u + 1) % STAGES), stB((u + 1) % STAGES), fan, fbn, AK, BK);
-        if constexpr (FOLD_OK)
+        read_phase(stA((u + 1) % STAGES), stB((u + 1) % STAGES), fan, fbn, DIAG, AK, BK, G0);
+        if constexpr (IS_DIAG)
+          fold_diag(stB((u + 1) % STAGES), std::integral_constant<int, (u + 1) % STAGES>{},
+                    kt / STAGES + (u == STAGES - 1 ? 1 : 0), G0);
+        else if constexpr (FOLD_OK)
           if (kt / STAGES + (u == STAGES - 1 ? 1 : 0) == fold_round)
             fold_c(stB((u + 1) % STAGES), std::integral_constant<int, (u + 1) % STAGES>{});
         phase_end();
@@ -792,17 +886,19 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
         auto& fa = fa0;
         auto& fb = fb0;
         if (kt + u >= 1) copy_my((u + 3) % STAGES, kclamp(kt + u + 3), BK);
-        read_frags(stA(u), stB(u), fa, fb, AK, BK);
-        if constexpr (FOLD_OK)
+        read_phase(stA(u), stB(u), fa, fb, DIAG, AK, BK, G1);
+        if constexpr (IS_DIAG)
+          fold_diag(stB(u), std::integral_constant<int, u>{}, kt / STAGES, G1);
+        else if constexpr (FOLD_OK)
           if (kt / STAGES == fold_round) fold_c(stB(u), std::integral_constant<int, u>{});
         phase_end();
-        mfma_phase(fa, fb, HALF);
+        mfma_phase(fa, fb, DIAG, G1);
         phase_end();
       });
     }
   }
   };
-  if (half_cols) k_loop(std::true_type{}, std::false_type{}, std::false_type{});
+  if (diag) k_loop(std::true_type{}, std::false_type{}, std::false_type{});
   else if (d.a_kmajor) k_loop(std::false_type{}, std::true_type{}, std::false_type{});
   else if (d.b_kmajor) k_loop(std::false_type{}, std::false_type{}, std::true_type{});
   else k_loop(std::false_type{}, std::false_type{}, std::false_type{});
@@ -832,7 +928,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
                                         static_cast<_Float16*>(d.D), d.ldd, d.D2);
     else
       epilogue_tile<C, EPI_SYM_DIAG>(acc, e, smem, sdiag, lane, wm, wn, m0, n0, nullptr, 0,
-                                     nullptr, half_cols);
+                                     nullptr);
   } else if (d.out_type == OUT_F16 && d.valid_m == M && d.valid_n == N && row_store_ok &&
              !d.D2 && (!e.C || d.c_type == OUT_F16)) {
     if (e.C)
