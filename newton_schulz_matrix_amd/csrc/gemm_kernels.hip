@@ -780,9 +780,10 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
       else seq(std::integral_constant<int, 0>{});
     }
   };
-  // acc[I][J] += rho * C for the 32 rows of block I, read from slice SB:
-  // lane l needs rows 8g + 4(l/32) .. +3 (g = 0..3) of column l%32 of block
-  // J, i.e. four consecutive k of B row (block J column), 8 bytes.
+  // a += rho * C for one 32 x 32 block whose rows arrive with slice SB and
+  // whose columns start at col0: lane l needs rows 8g + 4(l/32) .. +3
+  // (g = 0..3) of column col0 + l%32, i.e. four consecutive k of that B row,
+  // 8 bytes. fold_c applies it to the wave's blocks of row block I.
   auto fold_block = [&](const _Float16* SB, int col0, floatx16& a) {
     const int row = col0 + (lane & 31);
     const _Float16* base = SB + row * C::BK + 4 * (lane >> 5);

@@ -44,9 +44,14 @@ def test_no_gpu_fails_loudly():
 
 def test_traffic_only_for_the_profiled_source(tmp_path, monkeypatch):
     v = bench.gemm_traffic_per_launch()
-    assert v is None or v > 0
-    changed = tmp_path / "gemm_kernels.hip"
-    changed.write_bytes(open(bench.GEMM_SRC, "rb").read() + b"\n// edited\n")
+    assert v is not None and v > 0      # the committed profile matches the source
+    src = open(bench.GEMM_SRC, "rb").read()
+    commented = tmp_path / "commented.hip"
+    commented.write_bytes(src + b"\n// a comment\n   \n")
+    monkeypatch.setattr(bench, "GEMM_SRC", str(commented))
+    assert bench.gemm_traffic_per_launch() == v   # comments do not change the code
+    changed = tmp_path / "changed.hip"
+    changed.write_bytes(src.replace(b"constexpr int STAGES = 4;", b"constexpr int STAGES = 5;"))
     monkeypatch.setattr(bench, "GEMM_SRC", str(changed))
     assert bench.gemm_traffic_per_launch() is None
 
