@@ -351,7 +351,9 @@ ns_status ns_gemm_grouped(const ns_gemm_problem* probs, int count, int tile_edge
  * kernel of the plan can read or write, derived from its descriptors the
  * way the kernels address memory, must lie inside one workspace buffer of
  * the plan's layout or one caller matrix, with write permission where it is
- * written. ws_bytes == 0 takes the required size. `plant` != 0 first plants
+ * written; and each GEMM launch's workgroups must be dealt one-to-one onto
+ * its tiles.
+ * ws_bytes == 0 takes the required size. `plant` != 0 first plants
  * one of these mistakes into the plan, so a test can see the check catch it
  * (NS_ERR_UNSUPPORTED if the plan has no place for it):
  *   1 a caller's C read over the whole padded tile instead of its real block
@@ -361,6 +363,7 @@ ns_status ns_gemm_grouped(const ns_gemm_problem* probs, int count, int tile_edge
  *   5 the norm pass reading one row past the input
  *   6 a shard reduction running one block past its parts
  *   7 a product reading its K-major operand from one K block further on
+ *   8 the tile deal of a launch claiming one tile more than the launch has
  * Returns NS_OK, NS_ERR_INTERNAL (first violation described in msg, if msg
  * is not NULL, truncated to msg_len bytes), or the status the entry point's
  * argument checks give. */

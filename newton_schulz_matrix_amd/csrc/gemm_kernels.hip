@@ -37,7 +37,10 @@
 //     (row / 4) % 4 so the 16 lanes served per cycle by a 128-bit LDS read
 //     (16 consecutive rows) hit 16 distinct bank groups;
 //   * workgroup ids are remapped so each XCD (8 per MI355X, one L2 each)
-//     works on runs of 32 neighbouring tiles that share operand panels;
+//     works on runs of 32 neighbouring tiles that share operand panels, and
+//     every XCD gets the same share of the tiles of each K (deal_tile); the
+//     last tiles of a launch are claimed from a pool instead, so the XCDs
+//     that run faster do more of them;
 //   * either operand may instead be K-major (stored K x width in the
 //     row-pair layout, see km_off): X serves as the right operand of Q X,
 //     or as the left one of X^T Q, without a transposed copy; its slices
@@ -119,19 +122,6 @@ __device__ __forceinline__ uint32_t lds_addr_of(const _Float16* p) {
 // s_waitcnt immediate (gfx9): vmcnt in bits [3:0] and [15:14]; expcnt and
 // lgkmcnt left at their maxima, i.e. only vector-memory completions waited.
 constexpr int vmcnt_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
-
-// Workgroup id -> logical tile. Hardware hands workgroups to the 8 XCDs
-// round-robin (id % 8). Logical tiles are cut into chunks of 32; chunk c
-// goes to XCD c % 8, so each XCD walks its own run of 32 consecutive
-// logical tiles while the global order of chunks (largest problems first)
-// is kept. Identity on the ragged tail beyond the last multiple of 256.
-__device__ __forceinline__ int xcd_remap(int wg, int total) {
-  const int full = (total / 256) * 256;
-  if (wg >= full) return wg;
-  const int xcd = wg & 7, j = wg >> 3;
-  const int chunk = (j >> 5) * 8 + xcd;
-  return chunk * 32 + (j & 31);
-}
 
 // Logical tile of a full problem -> (ti, tj): bands of 4 tile rows, walked
 // column by column, so 32 consecutive tiles span 4 A panels and 8 B panels.
@@ -585,7 +575,8 @@ __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Flo
 
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
-    const GemmDesc* __restrict__ descs, int count, int total_tiles) {
+    const GemmDesc* __restrict__ descs, int count, int total_tiles, TileDeal deal,
+    int pool_begin, int* __restrict__ pool_claims) {
 #if defined(__HIP_DEVICE_COMPILE__)
   // Four stages as distinct LDS objects (the loop below is unrolled by four).
   // One LDS block: during the K loop, four stages of (A slice, B slice);
@@ -596,15 +587,41 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   auto stA = [&](int s) { return smem + s * (C::A_ELEMS + C::B_ELEMS); };
   auto stB = [&](int s) { return smem + s * (C::A_ELEMS + C::B_ELEMS) + C::A_ELEMS; };
 
-  const int t_logical = xcd_remap(blockIdx.x, total_tiles);
+  // Tiles [0, pool_begin) are dealt to the first pool_begin workgroups
+  // (deal_tile); the rest form a pool that the later workgroups claim in
+  // order, so the XCDs that get through their dealt tiles sooner (their
+  // clocks and memory paths differ by a few per cent) take more of the pool
+  // instead of waiting for the slowest at the end of the launch. The launch
+  // has a few more workgroups than tiles, so that a fast XCD has claimers to
+  // spare; a claimer that finds the pool empty ends at once.
+  int t_logical;
+  if (static_cast<int>(blockIdx.x) < pool_begin) {
+    t_logical = deal_tile(blockIdx.x, pool_begin, deal);
+  } else {
+    __shared__ int s_claim;
+    if (threadIdx.x == 0) s_claim = pool_begin + atomicAdd(pool_claims, 1);
+    __syncthreads();
+    t_logical = __builtin_amdgcn_readfirstlane(s_claim);
+    if (t_logical >= total_tiles) return;
+  }
   const int p = find_problem(descs, count, t_logical);
   const GemmDesc& d = descs[p];
+  // Everything the first copies need, read here in one go (adjacent fields,
+  // one batch of scalar loads and one wait) rather than one field at a time
+  // at its first use.
+  const _Float16* const dA = d.A;
+  const _Float16* const dB = d.B;
   const int t = t_logical - d.tile_begin;
+  const int tiles_n = d.tiles_n;
   const int M = d.M, N = d.N, K = d.K;
   const bool sym = d.symmetric != 0;
+  const int c_is_bt = d.c_is_bt;
+  const int a_pairs = d.a_pairs, b_pairs = d.b_pairs;
+  const int a_kmajor = d.a_kmajor, b_kmajor = d.b_kmajor;
+  const float alpha = d.alpha, beta = d.beta;
   int ti, tj;
-  if (sym) decode_lower(t, d.tiles_n, ti, tj);
-  else decode_full(t, M / C::BM, d.tiles_n, ti, tj);
+  if (sym) decode_lower(t, tiles_n, ti, tj);
+  else decode_full(t, M / C::BM, tiles_n, ti, tj);
   const int m0 = ti * C::BM, n0 = tj * C::BN;
 
   const int tid = threadIdx.x;
@@ -622,17 +639,20 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   // m0 / BK + wm * FM + I. With WM == STAGES * BK that slice sits in ring
   // position I of ring round m0 / (STAGES * BK) + wm.
   static_assert(C::FM == STAGES && C::WM == STAGES * C::BK, "fold: one ring round per wave");
-  const bool fold = d.c_is_bt != 0 && !d.b_kmajor;   // the fold reads row-major B slices
-  const float rho = fold ? d.beta / d.alpha : 0.f;
+  const bool fold = c_is_bt != 0 && !b_kmajor;   // the fold reads row-major B slices
+  const float rho = fold ? beta / alpha : 0.f;
   const int fold_round = fold ? m0 / (STAGES * C::BK) + wm : -1;
 
+  // zeroed once the first copies are on their way (see k_loop)
   floatx16 acc[C::FM][C::FN];
-  static_for<0, C::FM>([&](auto I) {
-    static_for<0, C::FN>([&](auto J) {
+  auto zero_acc = [&]() {
+    static_for<0, C::FM>([&](auto I) {
+      static_for<0, C::FN>([&](auto J) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[I][J][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[I][J][r] = 0.f;
+      });
     });
-  });
+  };
 
   // Copies. The four waves of group 0 (tile rows 0-127) copy every A slice
   // and the four of group 1 every B slice. Each wave instruction fills 1 KB
@@ -650,14 +670,14 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   static_assert(C::WAVES_M == 2 && COPIES == 4, "ping-pong plan: two groups of four waves");
   static_assert(C::A_ELEMS == 16 * 2 * C::BM, "K-major slice: 16 pairs of k rows per slice");
   const int grp = wm, gw = wn;
-  const bool my_pairs = (grp == 0 ? d.a_pairs : d.b_pairs) != 0;
-  const bool my_km = (grp == 0 ? d.a_kmajor : d.b_kmajor) != 0;
+  const bool my_pairs = (grp == 0 ? a_pairs : b_pairs) != 0;
+  const bool my_km = (grp == 0 ? a_kmajor : b_kmajor) != 0;
   const int64_t my_width = grp == 0 ? M : N;        // leading dimension if K-major
-  const _Float16* const my_km_base = grp == 0 ? d.A + 2 * static_cast<int64_t>(m0)
-                                              : d.B + 2 * static_cast<int64_t>(n0);
+  const _Float16* const my_km_base = grp == 0 ? dA + 2 * static_cast<int64_t>(m0)
+                                              : dB + 2 * static_cast<int64_t>(n0);
   const uint32_t panel_bytes = static_cast<uint32_t>(C::BM) * K * 2u;
-  const i32x4 rMy = grp == 0 ? make_rsrc(d.A + static_cast<int64_t>(m0) * K, panel_bytes)
-                             : make_rsrc(d.B + static_cast<int64_t>(n0) * K, panel_bytes);
+  const i32x4 rMy = grp == 0 ? make_rsrc(dA + static_cast<int64_t>(m0) * K, panel_bytes)
+                             : make_rsrc(dB + static_cast<int64_t>(n0) * K, panel_bytes);
   const uint32_t kbytes = my_pairs ? 4u : 2u;
   uint32_t my_off[COPIES];
   static_for<0, COPIES>([&](auto i) {
@@ -850,6 +870,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   constexpr bool FOLD_OK = !decltype(BK)::value;
   if (grp == 0) static_for<0, STAGES>([&](auto s) { copy_my(s, kclamp(s), AK); });
   else static_for<0, STAGES>([&](auto s) { copy_my(s, kclamp(s), BK); });
+  zero_acc();
   // only slice 0 is read before the next wait; slices 1-3 keep streaming
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * COPIES) & ~0x0F00);
   __builtin_amdgcn_s_barrier();
@@ -900,15 +921,15 @@ __global__ __launch_bounds__(C::THREADS) void gemm_nt_kernel(
   }
   };
   if (diag) k_loop(std::true_type{}, std::false_type{}, std::false_type{});
-  else if (d.a_kmajor) k_loop(std::false_type{}, std::true_type{}, std::false_type{});
-  else if (d.b_kmajor) k_loop(std::false_type{}, std::false_type{}, std::true_type{});
+  else if (a_kmajor) k_loop(std::false_type{}, std::true_type{}, std::false_type{});
+  else if (b_kmajor) k_loop(std::false_type{}, std::false_type{}, std::true_type{});
   else k_loop(std::false_type{}, std::false_type{}, std::false_type{});
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));   // trailing copies
   __builtin_amdgcn_s_barrier();
 
   // ---------------------------------------------------------------- epilogue
   Epi e;
-  e.alpha = d.alpha; e.beta = d.beta; e.gamma = d.gamma; e.delta = d.delta;
+  e.alpha = alpha; e.beta = beta; e.gamma = d.gamma; e.delta = d.delta;
   e.C = fold ? nullptr : d.C;   // folded C is already in the accumulators
   e.ldc = d.ldc; e.c_type = d.c_type;
   e.D = d.D; e.D2 = d.D2; e.DT = d.DT;
@@ -1194,11 +1215,12 @@ hipError_t launch_gemm_small(const GemmDesc* descs, int count, int total_tiles, 
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmDesc* descs, int count, int total_tiles,
-                       hipStream_t stream) {
+hipError_t launch_gemm(const GemmDesc* descs, int count, int total_tiles, const GemmCtl& ctl,
+                       int* pool_claims, hipStream_t stream) {
   if (total_tiles <= 0 || count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_nt_kernel<MainCfg>, dim3(total_tiles), dim3(MainCfg::THREADS),
-                     0, stream, descs, count, total_tiles);
+  hipLaunchKernelGGL(gemm_nt_kernel<MainCfg>, dim3(total_tiles + ctl.surplus),
+                     dim3(MainCfg::THREADS), 0, stream, descs, count, total_tiles, ctl.deal,
+                     ctl.pool_begin, pool_claims);
   return hipGetLastError();
 }
 

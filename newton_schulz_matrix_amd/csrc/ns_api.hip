@@ -206,6 +206,8 @@ struct Stage {
   int total;    // workgroups (chunks / tiles)
   bool small = false;   // GEMM on 64 x 64 tiles
   bool kmajor = false;  // GEMM with a K-major operand in some descriptor
+  GemmCtl ctl{};        // GEMM on 256 x 256 tiles: how its tiles are handed out
+  size_t claims_off = 0;  // GEMM on 256 x 256 tiles: its pool counter in the table
   double work;  // algorithmic flops (GEMM) or HBM bytes (normalisation)
 };
 
@@ -338,6 +340,73 @@ void layout(Plan& pl, const ns_matrix* mats, int count, ns_backend be, int shard
 
 void set_tiles(GemmDesc& d, int T);
 
+struct Arranged {
+  int total = 0;        // tiles of the launch
+  bool small = false;   // 64 x 64 tile kernel
+  bool kmajor = false;  // some descriptor has a K-major operand
+  GemmCtl ctl{};        // 256 x 256 kernel: dealt tiles, pool, surplus workgroups
+};
+
+// The pool of a 256 x 256 launch: its last tiles, about POOL_WORK of the
+// launch's work (a tile's work is its K), claimed in order by whichever
+// workgroups get there first; SURPLUS_FRACTION more workgroups than tiles
+// give the faster XCDs claimers to spare. Measured on MI355X, XCDs differ
+// by up to ~5% in the time they take for the same tiles; the sizes let a
+// fast XCD take that much more of the pool. Launches of fewer than
+// POOL_MIN_TILES tiles have no pool.
+constexpr double POOL_WORK = 0.15;
+constexpr double SURPLUS_FRACTION = 0.05;
+constexpr int POOL_MIN_TILES = 512;
+
+// Orders the problems of one grouped launch and numbers their tiles:
+// problems by K, longest first (the longest-processing-time rule: long
+// tiles start early, short ones fill the tail), then by tile count. A launch
+// of fewer than SMALL_STAGE_TILES tiles of 256 x 256 (too few to occupy the
+// chip) runs on the 64 x 64 tile kernel (force_edge overrides the rule);
+// both kernels give the same bits. On the 256 x 256 kernel the last tiles
+// form the claimed pool, and the runs of equal K before it become the
+// segments by which deal_tile spreads each K class evenly over the XCDs.
+Arranged arrange_gemm(std::vector<GemmDesc>& v, int force_edge) {
+  Arranged a;
+  std::stable_sort(v.begin(), v.end(), [](const GemmDesc& x, const GemmDesc& y) {
+    if (x.K != y.K) return x.K > y.K;
+    return x.tiles > y.tiles;
+  });
+  int big = 0;
+  for (auto& d : v) big += d.tiles;
+  a.small = force_edge ? force_edge == gemm_small_tile() : big < SMALL_STAGE_TILES;
+  double work = 0.0;
+  for (auto& d : v) {
+    if (a.small) set_tiles(d, gemm_small_tile());
+    d.tile_begin = a.total;
+    a.total += d.tiles;
+    a.kmajor = a.kmajor || d.a_kmajor || d.b_kmajor;
+    work += double(d.K) * d.tiles;
+  }
+  if (a.small) return a;
+  // the pool: the shortest suffix of the tile order holding POOL_WORK of the work
+  int pool_begin = a.total;
+  if (a.total >= POOL_MIN_TILES) {
+    double rest = POOL_WORK * work;
+    for (auto it = v.rbegin(); it != v.rend() && rest > 0.0; ++it) {
+      const int take = std::min(it->tiles, static_cast<int>(std::ceil(rest / it->K)));
+      pool_begin -= take;
+      rest -= double(take) * it->K;
+    }
+    a.ctl.surplus = (static_cast<int>(std::ceil(SURPLUS_FRACTION * a.total)) + 7) / 8 * 8;
+  }
+  a.ctl.pool_begin = pool_begin;
+  // deal segments: runs of equal K within the dealt tiles [0, pool_begin)
+  int n = 0;
+  for (size_t i = 0; i < v.size() && v[i].tile_begin < pool_begin; ++i) {
+    // past the segment limit, the rest joins the last segment
+    if ((i == 0 || v[i].K != v[i - 1].K) && n < MAX_DEAL_SEGS) a.ctl.deal.tiles[n++] = 0;
+    a.ctl.deal.tiles[n - 1] += std::min(v[i].tiles, pool_begin - v[i].tile_begin);
+  }
+  a.ctl.deal.count = n;
+  return a;
+}
+
 struct Builder {
   Plan& pl;
   unsigned char* ws;   // device base (may be null while sizing)
@@ -359,31 +428,20 @@ struct Builder {
     pl.stages.push_back(st);
   }
 
-  // One grouped GEMM launch; problems ordered by tile cost (K), largest
-  // first, so long tiles start early and short ones fill the tail. A stage
-  // with fewer than SMALL_STAGE_TILES 256-tiles (too few to occupy the
-  // chip) runs on 64 x 64 tiles instead; both kernels give the same bits.
+  // One grouped GEMM launch (see arrange_gemm).
   void gemm_stage(Probs pr, int force_edge = 0) {
     std::vector<GemmDesc>& v = pr.d;
-    std::stable_sort(v.begin(), v.end(), [](const GemmDesc& a, const GemmDesc& b) {
-      if (a.K != b.K) return a.K > b.K;
-      return a.tiles > b.tiles;
-    });
-    int big = 0;
-    for (auto& d : v) big += d.tiles;
-    const bool small = force_edge ? force_edge == gemm_small_tile() : big < SMALL_STAGE_TILES;
-    int begin = 0;
-    for (auto& d : v) {
-      if (small) set_tiles(d, gemm_small_tile());
-      d.tile_begin = begin;
-      begin += d.tiles;
-    }
-    bool km = false;
-    for (auto& d : v) km = km || d.a_kmajor || d.b_kmajor;
-    push(Stage::GEMM, v, begin, pr.flops);
+    const Arranged a = arrange_gemm(v, force_edge);
+    push(Stage::GEMM, v, a.total, pr.flops);
     if (!v.empty()) {
-      pl.stages.back().small = small;
-      pl.stages.back().kmajor = km;
+      Stage& st = pl.stages.back();
+      st.small = a.small;
+      st.kmajor = a.kmajor;
+      st.ctl = a.ctl;
+      if (!a.small) {   // the launch's pool counter, zero in every upload of the table
+        st.claims_off = align_up(pl.table.size(), 64);
+        pl.table.resize(st.claims_off + CLAIM_BYTES, 0);
+      }
     }
   }
 
@@ -892,6 +950,42 @@ bool check_gemm(const GemmDesc& d, Bounds& B, int T) {
   return B.err.empty();
 }
 
+// The tiles of one grouped launch: descriptor tile ranges back to back and,
+// on the 256 x 256 kernel, every tile handed out exactly once: deal_tile a
+// one-to-one map of the first pool_begin workgroups onto tiles
+// [0, pool_begin), the rest of the tiles left to the pool.
+bool check_deal(const GemmDesc* d, int count, int total, bool small, const GemmCtl& ctl,
+                Bounds& B) {
+  int next = 0;
+  for (int i = 0; i < count; ++i) {
+    if (d[i].tile_begin != next) return B.fail("gemm: tile ranges not contiguous");
+    next += d[i].tiles;
+  }
+  if (next != total) return B.fail("gemm: launch size differs from its tiles");
+  if (small) return true;
+  const int dealt = ctl.pool_begin;
+  if (dealt < 0 || dealt > total || ctl.surplus < 0 || (dealt == total && ctl.surplus != 0))
+    return B.fail("gemm: pool outside the launch");
+  const TileDeal& deal = ctl.deal;
+  if (deal.count < 0 || deal.count > MAX_DEAL_SEGS)
+    return B.fail("gemm: tile deal with a bad segment count");
+  if (deal.count > 0) {
+    int sum = 0;
+    for (int k = 0; k < deal.count; ++k) {
+      if (deal.tiles[k] < 1) return B.fail("gemm: empty tile deal segment");
+      sum += deal.tiles[k];
+    }
+    if (sum != dealt) return B.fail("gemm: tile deal segments do not cover the dealt tiles");
+  }
+  std::vector<char> seen(static_cast<size_t>(dealt), 0);
+  for (int wg = 0; wg < dealt; ++wg) {
+    const int t = deal_tile(wg, dealt, deal);
+    if (t < 0 || t >= dealt || seen[t]) return B.fail("gemm: tile deal is not one-to-one");
+    seen[t] = 1;
+  }
+  return true;
+}
+
 // Checks every descriptor of the plan; `ws` is the workspace base the plan
 // was built for.
 bool validate_plan(const Plan& pl, const unsigned char* ws, Bounds& B) {
@@ -903,15 +997,19 @@ bool validate_plan(const Plan& pl, const unsigned char* ws, Bounds& B) {
     switch (st.kind) {
       case Stage::GEMM: {
         const GemmDesc* d = reinterpret_cast<const GemmDesc*>(t);
-        int next = 0;
         for (int i = 0; i < st.count; ++i) {
-          if (d[i].tile_begin != next) return B.fail("gemm: tile ranges not contiguous");
-          next += d[i].tiles;
           if (st.small && !st.kmajor && (d[i].a_kmajor || d[i].b_kmajor))
             return B.fail("gemm: K-major operand in a launch of the row-major-only kernel");
           if (!check_gemm(d[i], B, st.small ? gemm_small_tile() : gemm_tile())) return false;
         }
-        if (next != st.total) return B.fail("gemm: launch size differs from its tiles");
+        if (!check_deal(d, st.count, st.total, st.small, st.ctl, B)) return false;
+        if (!st.small) {
+          int zero[CLAIM_BYTES / sizeof(int)] = {};
+          if (st.claims_off % 64 || st.claims_off < st.off ||
+              st.claims_off + CLAIM_BYTES > pl.table.size() ||
+              std::memcmp(pl.table.data() + st.claims_off, zero, CLAIM_BYTES) != 0)
+            return B.fail("gemm: pool counter outside the launch table or not zero");
+        }
         break;
       }
       case Stage::SUMSQ:
@@ -1029,6 +1127,7 @@ enum Plant {
   PLANT_SUMSQ_ROW = 5,      // the norm pass reads one row past G
   PLANT_REDUCE_TAIL = 6,    // a shard reduction runs one block past its parts
   PLANT_KMAJOR_K = 7,       // a K-major operand read from one K block further on
+  PLANT_DEAL_LONG = 8,      // a tile deal segment one tile longer than its tiles
 };
 bool plant_mistake(Plan& pl, const unsigned char* ws, size_t ws_bytes, int plant) {
   auto in_ws = [&](const void* p) {
@@ -1054,6 +1153,10 @@ bool plant_mistake(Plan& pl, const unsigned char* ws, size_t ws_bytes, int plant
         }
         if (plant == PLANT_K_OVERRUN) {
           g.K += gemm_k_multiple();
+          return true;
+        }
+        if (plant == PLANT_DEAL_LONG && !st.small && st.ctl.deal.count > 0) {
+          st.ctl.deal.tiles[0] += 1;
           return true;
         }
         if (plant == PLANT_KMAJOR_K && (g.a_kmajor || g.b_kmajor)) {
@@ -1162,7 +1265,8 @@ ns_status run_plan(const Plan& pl, unsigned char* ws, hipStream_t stream,
         e = timed(on, true, st.work, stream, [&] {
           const GemmDesc* d = reinterpret_cast<const GemmDesc*>(table + st.off);
           return st.small ? launch_gemm_small(d, st.count, st.total, st.kmajor, stream)
-                          : launch_gemm(d, st.count, st.total, stream);
+                          : launch_gemm(d, st.count, st.total, st.ctl,
+                                        reinterpret_cast<int*>(table + st.claims_off), stream);
         });
         break;
       case Stage::REDUCE:
@@ -1542,7 +1646,9 @@ NS_API ns_status ns_gemm_nt(const void* a, const void* b, const void* c, void* d
   g.tile_begin = 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (upload(ws, &g, sizeof(g), st) != hipSuccess) return NS_ERR_HIP;
-  if (launch_gemm(static_cast<const GemmDesc*>(ws), 1, g.tiles, st) != hipSuccess)
+  GemmCtl ctl{};   // every tile dealt (one segment), no pool
+  ctl.pool_begin = g.tiles;
+  if (launch_gemm(static_cast<const GemmDesc*>(ws), 1, g.tiles, ctl, nullptr, st) != hipSuccess)
     return NS_ERR_HIP;
   return NS_OK;
 }
@@ -1610,7 +1716,8 @@ ns_status grouped_desc(const ns_gemm_problem& q, GemmDesc& g) {
 
 NS_API ns_status ns_gemm_grouped_workspace_size(int count, size_t* bytes) {
   if (!bytes || count < 1) return NS_ERR_INVALID_ARG;
-  *bytes = align_up(static_cast<size_t>(count) * sizeof(GemmDesc) + 64);
+  // the descriptors, then the launch's pool counter
+  *bytes = align_up(align_up(static_cast<size_t>(count) * sizeof(GemmDesc), 64) + CLAIM_BYTES);
   return NS_OK;
 }
 
@@ -1632,27 +1739,23 @@ NS_API ns_status ns_gemm_grouped(const ns_gemm_problem* probs, int count, int ti
   if (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % ALIGN) return NS_ERR_WORKSPACE;
   const ns_status s = check_device();
   if (s != NS_OK) return s;
-  // the stage planner's order: longer K first, then more tiles
-  std::stable_sort(v.d.begin(), v.d.end(), [](const GemmDesc& a, const GemmDesc& b) {
-    if (a.K != b.K) return a.K > b.K;
-    return a.tiles > b.tiles;
-  });
-  int big = 0;
-  for (auto& d : v.d) big += d.tiles;
-  const bool small = tile_edge ? tile_edge == gemm_small_tile() : big < SMALL_STAGE_TILES;
-  int begin = 0;
-  bool km = false;
-  for (auto& d : v.d) {
-    if (small) set_tiles(d, gemm_small_tile());
-    d.tile_begin = begin;
-    begin += d.tiles;
-    km = km || d.a_kmajor || d.b_kmajor;
-  }
+  // the stage planner's order and tile deal (arrange_gemm)
+  const Arranged a = arrange_gemm(v.d, tile_edge);
+  Bounds B;
+  if (!check_deal(v.d.data(), static_cast<int>(v.d.size()), a.total, a.small, a.ctl, B))
+    return NS_ERR_INTERNAL;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (upload(ws, v.d.data(), v.d.size() * sizeof(GemmDesc), st) != hipSuccess) return NS_ERR_HIP;
-  const GemmDesc* dd = static_cast<const GemmDesc*>(ws);
-  if ((small ? launch_gemm_small(dd, count, begin, km, st) : launch_gemm(dd, count, begin, st)) !=
-      hipSuccess)
+  // the descriptors, then the launch's pool counter (zero)
+  const size_t claims_off = align_up(v.d.size() * sizeof(GemmDesc), 64);
+  std::vector<unsigned char> bytes(claims_off + CLAIM_BYTES, 0);
+  std::memcpy(bytes.data(), v.d.data(), v.d.size() * sizeof(GemmDesc));
+  if (upload(ws, bytes.data(), bytes.size(), st) != hipSuccess) return NS_ERR_HIP;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  const GemmDesc* dd = reinterpret_cast<const GemmDesc*>(w);
+  const int n = static_cast<int>(v.d.size());
+  if ((a.small ? launch_gemm_small(dd, n, a.total, a.kmajor, st)
+               : launch_gemm(dd, n, a.total, a.ctl, reinterpret_cast<int*>(w + claims_off),
+                             st)) != hipSuccess)
     return NS_ERR_HIP;
   return NS_OK;
 }

@@ -53,29 +53,89 @@ __host__ __device__ inline int64_t pair_index(int64_t i, int64_t j, int64_t ld) 
 // If symmetric: M == N, only tiles on or below the diagonal are computed
 // and every stored element (i, j), i >= j, is also stored at (j, i) in D
 // and D2, so both come out exactly symmetric.
+// The fields a tile needs before its first operand copies come first and
+// together (the kernel reads them in one batch of scalar loads); those only
+// the epilogue needs follow.
 struct GemmDesc {
   const _Float16* A;
   const _Float16* B;
+  int tile_begin;      // first logical tile of this problem in the launch
+  int tiles_n;         // full: N / BN ; symmetric: M / BM
+  int M, N, K;
+  int symmetric;
+  int c_is_bt;
+  int a_pairs, b_pairs;
+  int a_kmajor, b_kmajor;
+  float alpha, beta;
+  int tiles;           // number of tiles of this problem
   const void* C;       // may alias D (same element read then written)
   void* D;
   _Float16* D2;        // optional
   _Float16* DT;        // optional
-  int M, N, K;
   int ldd;
   int ldc;             // leading dimension of C (N for internal buffers)
   int c_type;          // OUT_F16 for internal buffers; any OutType for a caller's C
   int valid_m, valid_n;
   int diag_n;
   int out_type;
-  int symmetric;
-  int c_is_bt;
-  int a_pairs, b_pairs, c_pairs, d_pairs;
-  int a_kmajor, b_kmajor;
-  int tile_begin;      // first logical tile of this problem in the launch
-  int tiles;           // number of tiles of this problem
-  int tiles_n;         // full: N / BN ; symmetric: M / BM
-  float alpha, beta, gamma, delta;
+  int c_pairs, d_pairs;
+  float gamma, delta;
 };
+
+// Dealing the tiles of one 256 x 256 launch to the 8 XCDs. Hardware hands
+// workgroup w to XCD w % 8, and each XCD starts its workgroups in order.
+// The problems of a launch are ordered by K, longest first, and the launch's
+// logical tiles are cut into segments of equal K (equal tile cost). Within
+// a segment, whole rounds of 256 tiles go out as chunks of 32 neighbouring
+// tiles (chunk c of a round to XCD c % 8, so each XCD works on tiles that
+// share operand panels, and all XCDs on neighbouring chunks of the same
+// matrices); the rest of the segment is dealt as evenly as it can be: one
+// contiguous piece per XCD, the pieces one tile longer for the XCDs next in
+// turn. So every XCD gets the same share of every cost class (to one tile)
+// and the end of a long-K class is not left to a few XCDs.
+constexpr int MAX_DEAL_SEGS = 16;
+struct TileDeal {
+  int count;                    // segments; 0 = one segment of the whole launch
+  int tiles[MAX_DEAL_SEGS];     // tiles per segment, in logical order
+};
+
+// How one 256 x 256 launch hands out its tiles: tiles [0, pool_begin) are
+// dealt to workgroups 0 .. pool_begin - 1 by `deal` (over those tiles
+// only); tiles [pool_begin, total) form a pool that the remaining
+// workgroups claim in order with one atomic counter (zero at launch), and
+// `surplus` extra workgroups (which end at once if the pool is empty) let
+// the XCDs that run faster claim more of it. pool_begin == total: no pool.
+struct GemmCtl {
+  TileDeal deal;
+  int pool_begin;
+  int surplus;
+};
+
+// Logical tile of workgroup wg (0 <= wg < total) under deal `dl`; -1 if the
+// segments do not cover wg (a malformed deal: the host check refuses it).
+__host__ __device__ inline int deal_tile(int wg, int total, const TileDeal& dl) {
+  const int x = wg & 7;
+  int j = wg >> 3;               // this XCD's j-th workgroup
+  int start = 0, turn = 0;       // first tile of the segment, next XCD owed a longer piece
+  const int segs = dl.count > 0 ? dl.count : 1;
+  for (int s = 0; s < segs; ++s) {
+    const int n = dl.count > 0 ? dl.tiles[s] : total;
+    const int rounds = n >> 8, rest = n & 255;
+    if (j < rounds * 32) return start + (((j >> 5) << 3) + x) * 32 + (j & 31);
+    j -= rounds * 32;
+    const int q = rest >> 3, e = rest & 7;
+    const int mine = q + (((x - turn) & 7) < e ? 1 : 0);
+    if (j < mine) {
+      int off = start + rounds * 256 + q * x;
+      for (int y = 0; y < x; ++y) off += ((y - turn) & 7) < e ? 1 : 0;
+      return off + j;
+    }
+    j -= mine;
+    start += n;
+    turn = (turn + e) & 7;
+  }
+  return -1;
+}
 
 // Normalisation of one matrix G (m x n, leading dim ldg, dtype g_type):
 // x = fp16(g / (||G||_F + eps)). The padded region [0, pm) x [0, pn) in G's
@@ -152,8 +212,11 @@ hipError_t launch_norm_finalize(const NormDesc* descs, int count,
                                 hipStream_t stream);
 hipError_t launch_cast(const NormDesc* descs, int count, int total_tiles,
                        hipStream_t stream);
-hipError_t launch_gemm(const GemmDesc* descs, int count, int total_tiles,
-                       hipStream_t stream);
+// pool_claims: the launch's pool counter in device memory, zero at launch
+// (each launch needs its own; unused without a pool).
+hipError_t launch_gemm(const GemmDesc* descs, int count, int total_tiles, const GemmCtl& ctl,
+                       int* pool_claims, hipStream_t stream);
+constexpr int CLAIM_BYTES = 64;   // room for one launch's pool counter
 // The same products on 64 x 64 tiles (tile counts and tile_begin of the
 // descriptors in units of 64 x 64 tiles, symmetric problems as the rows of
 // their lower triangle); bitwise the same results as launch_gemm. kmajor:

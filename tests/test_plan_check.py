@@ -13,7 +13,9 @@ a plan built for plain addresses, so it can run here:
 * each of the planted mistakes (a caller's C read over the padded tile, the
   class of the fault once seen on a 300 x 700 Muon parameter; an unclipped
   output store; a K overrun; a cast past its padded block; a norm pass past
-  the input; a shard reduction past its parts) is caught.
+  the input; a shard reduction past its parts; a K-major operand read from
+  one K block on; a tile deal that claims one tile more than the launch
+  has) is caught.
 
 Caller buffers are laid out back to back, so any overrun runs into a
 neighbouring buffer rather than into unmapped space.
@@ -30,7 +32,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(nsmi.LIB_PATH),
                                 reason="libnsmi.so not built")
 
 ES = {nsmi.NS_DT_F32: 4, nsmi.NS_DT_BF16: 2, nsmi.NS_DT_F16: 2}
-PLANTS = range(1, 8)
+PLANTS = range(1, 9)
 
 
 class Arena:
