@@ -312,9 +312,12 @@ __device__ __forceinline__ void epilogue_output(const Acc& acc, const Epi& e) {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-  const uint16_t ua = __builtin_bit_cast(uint16_t, static_cast<_Float16>(a));
-  const uint16_t ub = __builtin_bit_cast(uint16_t, static_cast<_Float16>(b));
-  return static_cast<uint32_t>(ua) | (static_cast<uint32_t>(ub) << 16);
+  // one v_cvt_pk_f16_f32: both values rounded to nearest even, as two
+  // separate conversions would round them
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 __device__ __forceinline__ float lo_h(uint32_t w) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
@@ -513,7 +516,8 @@ __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Flo
         lane_swap(x1, y1);
         const u32x4 out = {x0, x1, y0, y1};
         *(__attribute__((address_space(3))) u32x4*)(Sl + stage_off(lcol, (lrow0 >> 3) + g0 + h)) = out;
-        if constexpr (MODE != EPI_SYM_DIAG) {
+        // (the mirror of a symmetric tile is stored from the staging below)
+        if constexpr (MODE == EPI_FULL || MODE == EPI_FULL_C) {
           if (T) {   // transposed copy
             const int64_t off = lidx(e.d_pairs, col, rbase + 8 * (g0 + h), ldT);
             *gmem(reinterpret_cast<u32x4*>(T + off)) = out;
@@ -571,6 +575,26 @@ __device__ __forceinline__ void epilogue_tile(const Acc& acc, const Epi& e, _Flo
       }
     });
   });
+  // Mirror of an off-diagonal symmetric tile: row n0 + c of the output (c in
+  // this wave's 64 tile columns), columns m0 + (this wave's 128 tile rows),
+  // is this wave's staged column c as it stands. One instruction covers 4
+  // columns x 16 chunks: in the row-pair layout, two pairs of output rows
+  // over 128 columns, i.e. whole 128-byte lines (the same bytes stored
+  // straight from registers would fill only half of each line they touch).
+  // The 16 chunks of a column sit in one half of its swizzled slots, so a
+  // column's reads hit distinct banks.
+  if constexpr (MODE == EPI_SYM_OFFDIAG) {
+    if (T) {
+      static_for<0, Cf::WN / 4>([&](auto CB) {
+        const int c = wn * Cf::WN + CB * 4 + (lane >> 4);
+        const int k = wm * (Cf::WM / 8) + (lane & 15);
+        const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(Sl + stage_off(c, k));
+        const int64_t off = lidx(e.d_pairs, n0 + c, m0 + 8 * k, ldT);
+        *gmem(reinterpret_cast<u32x4*>(T + off)) = v;
+        if (T2) *gmem(reinterpret_cast<u32x4*>(T2 + off)) = v;
+      });
+    }
+  }
 }
 
 template <class C>
