@@ -7,9 +7,12 @@ row-pair layout of internal buffers, beta * C folded from the B slices
 start or restart, the transposed second output DT of the restart product,
 symmetric (lower-tile + mirror) mode, the clipped, typed epilogue that
 writes a caller's buffer, and K-major operands (X read as the right operand
-of Q X, or as the left operand of X^T Q, from its own row-pair buffer). Each launch holds more than 256 tiles, so the XCD
-remapping of workgroup ids and the banded tile walks (several bands of tile
-rows, lower-triangle bands for symmetric products) are all exercised. Shapes
+of Q X, or as the left operand of X^T Q, from its own row-pair buffer). Each
+launch holds more than 256 tiles, so the dealing of tiles to the XCDs and
+the banded tile walks (several bands of tile rows, lower-triangle bands for
+symmetric products) are all exercised; the launches of 896 tiles and more
+also have a claimed tail pool, and the K-major launch two K classes (two
+deal segments). Shapes
 are the Llama-3-8B owner batch's: SYRK 4096 x 14336, symmetric 4096^3 Gram-
 space products, Q X with Q 4096^2 and X 4096 x 14336, plus a ragged
 caller-buffer tail.
