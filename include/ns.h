@@ -39,7 +39,8 @@
  *               function reports, 256-byte aligned (NS_ERR_WORKSPACE
  *               otherwise), with no required contents: every call writes
  *               what it reads. The call also writes its launch descriptors
- *               there.
+ *               there, and the integer counters (reset by every call) with
+ *               which the workgroups of a launch claim its last tiles.
  *   Graphs      A call enqueues kernel launches only (its descriptor tables
  *               travel as kernel arguments of small fill launches; there are
  *               no host-to-device copies, memsets or host waits), so it can
@@ -56,7 +57,9 @@
  *   Device      The current HIP device must be a gfx950 GPU, otherwise
  *               NS_ERR_UNSUPPORTED.
  *   Determinism The same inputs on the same device give bitwise identical
- *               outputs: fixed tile and reduction order, no float atomics.
+ *               outputs: fixed tile and reduction order, no float atomics
+ *               (which workgroup computes a claimed tile varies from run to
+ *               run, how it is computed does not).
  *   Precision   Every stored intermediate is fp16; products accumulate in
  *               fp32; scalar epilogues are evaluated in fp32 and rounded
  *               once.
