@@ -60,6 +60,35 @@ def test_batched_call_replays_bitwise(backend):
             assert torch.equal(a, b), (rep, i, shapes[i])
 
 
+def test_large_launches_with_a_claimed_pool_replay_bitwise():
+    """Six 1024 x 4096 matrices and one 2048 x 8192: the restart and output
+    products run on the 256 x 256 kernel with 640 tiles each, so their
+    last tiles are claimed through a counter in the workspace, which every
+    replay must reset (a stale counter would leave those tiles unwritten)."""
+    require_gpu()
+    shapes = [(1024, 4096)] * 6 + [(2048, 8192)]
+    print(f"graph replay, claimed pool: {shapes}", flush=True)
+    Gs = [W.small_gaussian(120 + i, *sh).cuda() for i, sh in enumerate(shapes)]
+    outs = [torch.empty(G.shape, dtype=torch.float16, device="cuda") for G in Gs]
+    table = nsmi.POLAR_EXPRESS_COEFFICIENTS
+    ws = torch.empty(nsmi.ns_workspace_size(shapes, "gram", table, (2,)), dtype=torch.uint8,
+                     device="cuda")
+    g = _capture(lambda: nsmi.ns_batched(Gs, "gram", table, (2,), outs=outs, workspace=ws))
+    for rep in range(3):
+        for i, (G, sh) in enumerate(zip(Gs, shapes)):
+            G.copy_(W.small_gaussian(130 + 10 * rep + i, *sh).cuda())
+        for o in outs:
+            o.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [o.clone() for o in outs]
+        want = nsmi.ns_batched(Gs, "gram", table, (2,))
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(got, want)):
+            assert torch.equal(a, b), (rep, i, shapes[i])
+
+
 def test_single_matrix_workload_replays_bitwise():
     """The 256 x 1024 workload (Polar Express, restart [2]), both backends
     captured in one graph."""
